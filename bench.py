@@ -1,0 +1,226 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME --batch B]
+
+A step is one paged_attention_decode call (validation, plan, decode kernel and,
+for split plans, the partition-reduce kernel) over one synthetic batch already
+resident in HBM.  Prints ONE JSON line on stdout.
+
+value = algorithmic bytes per call / time per call (GB/s, decimal), where the
+algorithmic bytes are K and V of every context token once per kv head, q in,
+out back, one block-table entry per used block and the context lengths
+(plus the slopes with ALiBi).
+
+Caches are defeated by rotating over independent input sets whose combined
+footprint is at least 2 GiB (the headline workload alone is 4.3 GB, so it
+uses a single set).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor peak
+ROTATE_BYTES = 2 << 30          # >= 8x the 256 MB last-level cache
+METRIC = "paged-attn decode µs/call + achieved HBM GB/s (% of peak), GQA 64q/8kv bf16"
+# Context from the reference pages (A100-40GB-PCIE, bf16, 64q/8kv, ctx 4096,
+# batch 256): FlashAttention decode 2583.970 us, paged attention V1 8771.168 us.
+PAGES_US = {("gqa_ctx4096", 256): {"flash_attention_a100_us": 2583.970, "paged_v1_a100_us": 8771.168}}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def workload_label(name, args):
+    return (f"{name}: {args['num_heads']}q/{args['num_kv_heads']}kv heads, D={args['head_size']}, "
+            f"{args['dtype']}, block {args['block_size']}, batch {args['num_seqs']}, "
+            f"context {args['context_lens']}" + (", ALiBi" if args.get("alibi") else ""))
+
+
+def cpu_baseline(args, budget_s):
+    """The fp64 oracle on a bounded sample of the same workload, on the host cores."""
+    import numpy as np
+
+    import oracle
+    from workloads import algorithmic_bytes, decode_inputs, raw_u16
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    sample_args = dict(args)
+    n = min(args["num_seqs"], 64)
+    sample_args["num_seqs"] = n
+    inp = decode_inputs(device="cpu", **sample_args)
+    q, kc, vc = raw_u16(inp.query), raw_u16(inp.key_cache), raw_u16(inp.value_cache)
+    tables, lens = inp.block_tables.numpy(), inp.context_lens.numpy()
+    slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.numpy()
+    done = []
+    t0 = time.perf_counter()
+    for s in range(n):
+        oracle.paged_decode(q, kc, vc, tables, lens, inp.scale, inp.block_size, slopes,
+                            dtype=inp.dtype, seqs=[s])
+        done.append(s)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = algorithmic_bytes(context_lens=lens[done].tolist(), num_heads=args["num_heads"],
+                               num_kv_heads=args["num_kv_heads"], head_size=args["head_size"],
+                               block_size=args["block_size"], alibi=bool(args.get("alibi")))
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "sample": f"{len(done)} of {args['num_seqs']} sequences of the same workload "
+                      f"({dt:.1f} s wall, fp64 numpy)",
+            "seconds_per_sequence": round(dt / len(done), 4)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); the decode "
+              "kernel has no cross-GPU path to measure", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_attention_paged_06_amd import (make_dims, make_opts, paged_attention_decode,
+                                               paged_attention_plan)
+    from workloads import HEADLINE, algorithmic_bytes, algorithmic_flops, decode_inputs, workload_args
+
+    name = a.workload or HEADLINE[0]
+    batch = a.batch or HEADLINE[1]
+    args = workload_args(name, batch)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    first = decode_inputs(device=dev, **args)
+    lens = first.context_lens.cpu().tolist()
+    nbytes = algorithmic_bytes(context_lens=lens, num_heads=args["num_heads"],
+                               num_kv_heads=args["num_kv_heads"], head_size=args["head_size"],
+                               block_size=args["block_size"], alibi=bool(args.get("alibi")))
+    flops = algorithmic_flops(context_lens=lens, num_heads=args["num_heads"],
+                              head_size=args["head_size"])
+    footprint = sum(t.numel() * t.element_size() for t in
+                    (first.query, first.key_cache, first.value_cache, first.block_tables))
+    nsets = max(1, -(-ROTATE_BYTES // footprint))
+    sets = [first]
+    for i in range(1, nsets):
+        # same lengths and shapes, fresh values and block assignment
+        sets.append(decode_inputs(device=dev, **dict(args, seed=args["seed"] + 100000 * i)))
+    outs = [torch.empty_like(s.query) for s in sets]
+
+    dims = make_dims(first.query, first.key_cache, first.block_tables)
+    opts = make_opts(a.partition_size, a.engine)
+    plan = paged_attention_plan(dims, 1 << 40, opts)
+    workspace = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+                 if plan.workspace_bytes else None)
+
+    def step(i):
+        s = sets[i % nsets]
+        paged_attention_decode(outs[i % nsets], s.query, s.key_cache, s.value_cache,
+                               s.block_tables, s.context_lens, s.scale, s.block_size,
+                               s.alibi_slopes, workspace=workspace,
+                               partition_size=a.partition_size, engine=a.engine)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(a.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(a.steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    per_call_ms = [s.elapsed_time(e) for s, e in ev]
+    avg_ms = sum(per_call_ms) / len(per_call_ms)
+    region_ms = t_start.elapsed_time(t_end)
+    ms_per_step = region_ms / a.steps
+    gbps = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+
+    context = PAGES_US.get((name, batch))
+    vs = None
+    if context:
+        vs = round(context["flash_attention_a100_us"] / (ms_per_step * 1e3), 3)
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": vs,
+        "dtype": args["dtype"],
+        "data": "synthetic",
+        "config": {
+            "workload": workload_label(name, args),
+            "num_seqs": batch, "num_heads": args["num_heads"], "num_kv_heads": args["num_kv_heads"],
+            "head_size": args["head_size"], "block_size": args["block_size"],
+            "context_lens": str(args["context_lens"]), "seed": args["seed"],
+            "engine": {0: "auto", 1: "valu", 2: "mfma"}[plan.engine] if a.engine == "auto" else a.engine,
+            "num_partitions": plan.num_partitions, "partition_size": plan.partition_size,
+            "input_sets_rotated": nsets,
+        },
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "algorithmic_bytes_per_call": nbytes,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel": "decode_mfma_kernel" if plan.engine == 2 else "decode_valu_kernel",
+            "kernel_avg_us": round(avg_ms * 1e3, 2),
+            "flops_per_call": flops,
+            "note": ("per-call HIP events on the launch stream; one decode kernel per call"
+                     if plan.num_partitions == 1 else
+                     "per-call HIP events include the partition-reduce kernel"),
+        },
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if context:
+        result["pages_context"] = dict(context, note="A100 numbers from the reference pages; "
+                                       "vs_baseline = FlashAttention A100 us / this us")
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,10 @@
+"""Paged decode attention for AMD Instinct MI355X (gfx950).
+
+The computation lives in the HIP kernels of ``libpagedattn.so`` behind the C
+ABI of ``include/paged_attention.h``; this package only marshals arguments.
+"""
+from .ops import (gather_cached_kv, make_dims, make_opts, paged_attention_decode,
+                  paged_attention_plan, paged_attention_workspace_bytes)
+
+__all__ = ["gather_cached_kv", "make_dims", "make_opts", "paged_attention_decode",
+           "paged_attention_plan", "paged_attention_workspace_bytes"]

@@ -1,0 +1,295 @@
+// C-ABI host layer: argument validation, the launch planner, workspace sizing,
+// dispatch and error reporting.  See include/paged_attention.h for the
+// contract.  Nothing here reads device memory or synchronises a stream.
+#include "paged_attention.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return PA_OK;
+}
+
+constexpr size_t kWsAlign = 256;
+constexpr int kMaxDevices = 64;
+// Workgroups per CU the auto plan aims for before it splits contexts.
+constexpr int kTargetGroupsPerCu = 2;
+// Smallest partition the auto plan makes: two blocks per wave.
+constexpr int kMinPartitionBlocks = 2 * pa::kWaves;
+
+std::atomic<int> g_num_cus[kMaxDevices];
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_dims(const pa_dims* d) {
+  if (d == nullptr) return fail(PA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->num_seqs < 0 || d->num_seqs > 65535)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs = %d (must be in [0, 65535])", d->num_seqs);
+  if (d->num_heads <= 0 || d->num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_heads = %d, num_kv_heads = %d (must be positive)",
+                d->num_heads, d->num_kv_heads);
+  if (d->num_heads % d->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_heads (%d) is not a multiple of num_kv_heads (%d)",
+                d->num_heads, d->num_kv_heads);
+  if (d->num_heads / d->num_kv_heads > pa::kMaxGroup)
+    return fail(PA_ERR_UNSUPPORTED, "num_heads / num_kv_heads = %d exceeds %d",
+                d->num_heads / d->num_kv_heads, pa::kMaxGroup);
+  if (d->dtype != PA_F16 && d->dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "dtype %d (expected PA_F16 or PA_BF16)", d->dtype);
+  if (d->head_size != 64 && d->head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_size %d (built for 64 and 128)", d->head_size);
+  if (d->block_size != pa::kBlockSize)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d (built for %d)", d->block_size,
+                pa::kBlockSize);
+  if (d->num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks = %d", d->num_blocks);
+  if (d->max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq = %d", d->max_blocks_per_seq);
+  if ((long long)d->max_blocks_per_seq * d->block_size > (1LL << 30))
+    return fail(PA_ERR_INVALID_ARG, "context bound max_blocks_per_seq * block_size too large");
+  return PA_OK;
+}
+
+int current_num_cus(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_DEVICE, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_DEVICE, "device index %d", dev);
+  int n = g_num_cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return fail(PA_ERR_DEVICE, "cannot query the compute-unit count of device %d", dev);
+    g_num_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  *out = n;
+  return PA_OK;
+}
+
+// Workspace bytes for P partitions: fp32 partial outputs, then (m, l) pairs.
+size_t split_workspace(const pa_dims* d, int P) {
+  if (P <= 1) return 0;
+  const size_t rows = (size_t)d->num_seqs * d->num_heads * P;
+  return align_up(rows * d->head_size * sizeof(float), kWsAlign) + rows * 2 * sizeof(float);
+}
+
+int resolve_engine(const pa_dims* d, const pa_opts* o, int* engine) {
+  int e = o ? o->engine : PA_ENGINE_AUTO;
+  if (e != PA_ENGINE_AUTO && e != PA_ENGINE_VALU && e != PA_ENGINE_MFMA)
+    return fail(PA_ERR_INVALID_ARG, "engine %d", e);
+  if (e == PA_ENGINE_AUTO) {
+    const int group = d->num_heads / d->num_kv_heads;
+    e = group >= 4 ? PA_ENGINE_MFMA : PA_ENGINE_VALU;
+  }
+  *engine = e;
+  return PA_OK;
+}
+
+// The planner.  `unlimited` ignores ws_bytes (used for sizing).
+int make_plan(const pa_dims* d, size_t ws_bytes, const pa_opts* o, bool unlimited, pa_plan* p) {
+  int st = check_dims(d);
+  if (st) return st;
+  int engine = 0;
+  if ((st = resolve_engine(d, o, &engine))) return st;
+  const int maxb = d->max_blocks_per_seq;
+  const int forced = o ? o->partition_size : 0;
+  int P = 1, PB = maxb;
+
+  if (forced == -1) {
+    P = 1;
+  } else if (forced > 0) {
+    if (forced % d->block_size != 0)
+      return fail(PA_ERR_INVALID_ARG, "partition_size %d is not a multiple of block_size %d",
+                  forced, d->block_size);
+    PB = forced / d->block_size;
+    P = (maxb + PB - 1) / PB;
+    if (P > 65535) return fail(PA_ERR_INVALID_ARG, "partition_size %d gives %d partitions", forced, P);
+    if (P > 1 && !unlimited && split_workspace(d, P) > ws_bytes)
+      return fail(PA_ERR_WORKSPACE, "forced partition_size %d needs %zu workspace bytes, got %zu",
+                  forced, split_workspace(d, P), ws_bytes);
+  } else if (forced == 0) {
+    int cus = o ? o->num_cus : 0;
+    if (cus < 0) return fail(PA_ERR_INVALID_ARG, "num_cus = %d", cus);
+    if (cus == 0 && (st = current_num_cus(&cus))) return st;
+    const int group = d->num_heads / d->num_kv_heads;
+    const long long chunks =
+        engine == PA_ENGINE_VALU
+            ? (group + pa::valu_heads_per_workgroup(group) - 1) / pa::valu_heads_per_workgroup(group)
+            : 1;
+    const long long units = (long long)d->num_seqs * d->num_kv_heads * chunks;
+    const long long target = (long long)kTargetGroupsPerCu * cus;
+    if (units > 0 && units < target && maxb > kMinPartitionBlocks) {
+      long long want = (target + units - 1) / units;
+      PB = (int)((maxb + want - 1) / want);
+      if (PB < kMinPartitionBlocks) PB = kMinPartitionBlocks;
+      P = (maxb + PB - 1) / PB;
+      // shrink to what the workspace holds
+      while (P > 1 && !unlimited && split_workspace(d, P) > ws_bytes) {
+        PB *= 2;
+        P = (maxb + PB - 1) / PB;
+      }
+    }
+  } else {
+    return fail(PA_ERR_INVALID_ARG, "partition_size %d (use 0, -1 or a positive multiple of %d)",
+                forced, d->block_size);
+  }
+  if (P <= 1) {
+    P = 1;
+    PB = maxb;
+  }
+  p->num_partitions = P;
+  p->partition_size = PB * d->block_size;
+  p->engine = engine;
+  p->reserved = 0;
+  p->workspace_bytes = split_workspace(d, P);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_ALIGNMENT: return "misaligned pointer";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_DEVICE: return "device query failed";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+int paged_attention_plan(const pa_dims* dims, size_t workspace_bytes, const pa_opts* opts,
+                         pa_plan* plan) {
+  if (plan == nullptr) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
+  pa_plan p;
+  const int st = make_plan(dims, workspace_bytes, opts, false, &p);
+  if (st) return st;
+  *plan = p;
+  return ok();
+}
+
+size_t paged_attention_workspace_bytes(const pa_dims* dims, const pa_opts* opts) {
+  pa_plan p;
+  if (make_plan(dims, 0, opts, true, &p)) return 0;
+  return p.workspace_bytes;
+}
+
+int paged_attention_decode(void* out, const void* query, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, float scale, int32_t block_size,
+                           const float* alibi_slopes, pa_stream_t stream, const pa_dims* dims,
+                           void* workspace, size_t workspace_bytes, const pa_opts* opts) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (block_size != dims->block_size)
+    return fail(PA_ERR_INVALID_ARG, "block_size argument %d differs from dims->block_size %d",
+                block_size, dims->block_size);
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (dims->num_seqs == 0) return ok();
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16))
+    return fail(PA_ERR_ALIGNMENT, "out, query and caches must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      (alibi_slopes && !aligned(alibi_slopes, 4)))
+    return fail(PA_ERR_ALIGNMENT, "block_tables, context_lens and alibi_slopes must be 4-byte aligned");
+
+  pa_plan plan;
+  if ((st = make_plan(dims, workspace ? workspace_bytes : 0, opts, false, &plan))) return st;
+  if (plan.num_partitions > 1) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "split plan needs a workspace");
+    if (!aligned(workspace, kWsAlign))
+      return fail(PA_ERR_ALIGNMENT, "workspace must be %zu-byte aligned", kWsAlign);
+  }
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.q = query;
+  a.k_cache = key_cache;
+  a.v_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.alibi = alibi_slopes;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = dims->num_seqs;
+  a.num_heads = dims->num_heads;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.max_blocks_per_seq = dims->max_blocks_per_seq;
+  a.group = dims->num_heads / dims->num_kv_heads;
+  a.num_partitions = plan.num_partitions;
+  a.partition_blocks = plan.partition_size / dims->block_size;
+  a.ws_o = nullptr;
+  a.ws_ml = nullptr;
+  if (plan.num_partitions > 1) {
+    const size_t rows = (size_t)dims->num_seqs * dims->num_heads * plan.num_partitions;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align_up(rows * dims->head_size * sizeof(float), kWsAlign));
+  }
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = plan.engine == PA_ENGINE_MFMA
+                     ? pa::launch_decode_mfma(a, dims->dtype, dims->head_size, s)
+                     : pa::launch_decode_valu(a, dims->dtype, dims->head_size, s);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
+  if (plan.num_partitions > 1) {
+    e = pa::launch_partition_reduce(a, dims->dtype, dims->head_size, s);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reduce launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
+                     const void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                     int32_t num_blocks, int32_t dtype, pa_stream_t stream) {
+  if (dtype != PA_F16 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (num_tokens < 0 || num_kv_heads <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_tokens %d, num_kv_heads %d, block_size %d, num_blocks %d",
+                num_tokens, num_kv_heads, block_size, num_blocks);
+  if (head_size <= 0 || head_size % 8 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "head_size %d (must be a positive multiple of 8)", head_size);
+  if ((unsigned long long)num_tokens * num_kv_heads * (head_size / 8) >= (1ULL << 32))
+    return fail(PA_ERR_INVALID_ARG, "num_tokens * num_kv_heads * head_size too large");
+  if ((unsigned long long)num_blocks * block_size > 0x7fffffffULL)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks * block_size exceeds the int32 slot range");
+  if (num_tokens == 0) return ok();
+  if (!key_out || !value_out || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(key_out, 16) || !aligned(value_out, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(slot_mapping, 4))
+    return fail(PA_ERR_ALIGNMENT, "16-bit tensors must be 16-byte aligned, slot_mapping 4-byte");
+  const hipError_t e = pa::launch_gather(key_out, value_out, key_cache, value_cache, slot_mapping,
+                                         num_tokens, num_kv_heads, head_size, block_size,
+                                         reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "gather launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,270 @@
+// Paged decode attention on the vector ALUs of gfx950.
+//
+// Operation: for one new query token per head, softmax(scale * q.K + alibi).V
+// over the sequence's cached tokens, reached through its block table ("single
+// query cached KV attention", vLLM PR #420; GQA head mapping of vLLM PR #452).
+//
+// Work decomposition
+//   workgroup = (kv head, query-head chunk of GT heads, sequence, partition),
+//   4 waves.  Wave w takes the partition's cache blocks w, w+4, w+8, ...
+//   The GT query heads that share the kv head are loaded once into LDS by the
+//   whole workgroup and every lane keeps its 16-byte slice in registers (the
+//   shared query load of vLLM PR #420, done per kv head so each K/V row read
+//   serves all GT heads).
+//
+// Lane layout inside a wave (D = head size)
+//   TPT = D/8 lanes cover one token row (16 bytes each), TPL = 64/TPT token
+//   rows per wave-wide 16-byte load, BS/TPL loads per 16-token block.  One
+//   load of K (or V) is fully coalesced: TPL consecutive rows of the
+//   contiguous [BS, D] block tile.
+//   q.k: each lane takes 4 packed dot2 products over its 8 elements, then a
+//   DPP row reduction (mirror / half-mirror / quad swaps) gives every lane of
+//   the row the full dot product -- no LDS, no wave-wide barrier.
+//   Every lane row keeps its own online-softmax state (running max m, sum l,
+//   fp32 accumulator of its 8 output elements per head), so no cross-row
+//   traffic happens inside the block loop.  Rows, then waves, are merged once
+//   at the end with the exact rescaling identity of the split softmax.
+#include "../launch.h"
+#include "device_common.h"
+
+namespace pa {
+
+template <typename Fmt, int D, int GT>
+__global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeArgs a) {
+  constexpr int BS = kBlockSize;
+  constexpr int CH = D / 8;        // 16-byte chunks per token row
+  constexpr int TPT = CH;          // lanes per token row
+  constexpr int TPL = 64 / TPT;    // token rows per wave-wide load
+  constexpr int NLOAD = BS / TPL;  // loads per block for K, and for V
+  static_assert(BS % TPL == 0, "block must hold a whole number of wave loads");
+  static_assert(64 % TPT == 0, "rows must tile the wave");
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rho = lane / TPT;   // token row of this lane within a load
+  const int c = lane % TPT;     // 16-byte chunk of the row
+
+  const int nhc = (a.group + GT - 1) / GT;
+  const int kvh = blockIdx.x / nhc;
+  const int hc = blockIdx.x - kvh * nhc;
+  const int seq = blockIdx.y;
+  const int part = blockIdx.z;
+  const int h0 = kvh * a.group + hc * GT;
+  const int nh = min(GT, a.group - hc * GT);
+  const bool single = a.num_partitions == 1;
+
+  const int L = min(a.context_lens[seq], a.max_blocks_per_seq * BS);
+  const int tok0 = part * a.partition_blocks * BS;
+  if (L <= 0) {
+    if (single) {
+      uint4* o = reinterpret_cast<uint4*>(a.out) + ((size_t)seq * a.num_heads + h0) * CH;
+      for (int i = threadIdx.x; i < nh * CH; i += kWaves * 64) o[i] = make_uint4(0, 0, 0, 0);
+    }
+    return;
+  }
+  if (tok0 >= L) return;  // partition past this sequence's end: nothing to do
+  const int tok1 = min(L, tok0 + a.partition_blocks * BS);
+  const int blk0 = tok0 / BS;
+  const int nblk = (tok1 - tok0 + BS - 1) / BS;
+
+  // ---- shared query load --------------------------------------------------
+  __shared__ uint4 q_lds[GT * CH];
+  {
+    const uint4* qg = reinterpret_cast<const uint4*>(a.q) + ((size_t)seq * a.num_heads + h0) * CH;
+    for (int i = threadIdx.x; i < GT * CH; i += kWaves * 64)
+      q_lds[i] = (i < nh * CH) ? qg[i] : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  uint32_t qv[GT][4];
+  float slope[GT];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    const uint4 t = q_lds[g * CH + c];
+    qv[g][0] = t.x; qv[g][1] = t.y; qv[g][2] = t.z; qv[g][3] = t.w;
+    slope[g] = (a.alibi != nullptr && g < nh) ? a.alibi[h0 + g] * kLog2e : 0.f;
+  }
+
+  float m[GT], l[GT], acc[GT][8];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    m[g] = kNegBig;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  }
+
+  // ---- block walk -----------------------------------------------------------
+  const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq + blk0;
+  const size_t bstride = (size_t)a.num_kv_heads * BS * CH;  // uint4 per physical block
+  const size_t lane_off = (size_t)kvh * BS * CH + rho * CH + c;
+  const uint4* kbase = reinterpret_cast<const uint4*>(a.k_cache) + lane_off;
+  const uint4* vbase = reinterpret_cast<const uint4*>(a.v_cache) + lane_off;
+  const int qpos = L - 1;  // position of the query token
+
+  for (int b = wave; b < nblk; b += kWaves) {
+    const int phys = table[b];
+    const uint4* kp = kbase + (size_t)phys * bstride;
+    const uint4* vp = vbase + (size_t)phys * bstride;
+    uint4 kr[NLOAD], vr[NLOAD];
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) kr[i] = load_nt(kp + i * TPL * CH);
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) vr[i] = load_nt(vp + i * TPL * CH);
+
+    const int tb = (blk0 + b) * BS;  // absolute position of the block's row 0
+    const int valid = tok1 - tb;     // rows [0, valid) are context tokens
+
+    float x[GT][NLOAD];
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+      const int row = i * TPL + rho;
+      const float rel = (float)(tb + row - qpos);
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float s = Fmt::dot2(kr[i].x, qv[g][0], 0.f);
+        s = Fmt::dot2(kr[i].y, qv[g][1], s);
+        s = Fmt::dot2(kr[i].z, qv[g][2], s);
+        s = Fmt::dot2(kr[i].w, qv[g][3], s);
+        s = group_sum<TPT>(s);
+        const float z = fmaf(s, a.scale_log2, slope[g] * rel);
+        x[g][i] = row < valid ? z : kNegBig;
+      }
+    }
+
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float mx = x[g][0];
+#pragma unroll
+      for (int i = 1; i < NLOAD; ++i) mx = fmaxf(mx, x[g][i]);
+      const float mn = fmaxf(m[g], mx);
+      const float alpha = fast_exp2(m[g] - mn);
+      m[g] = mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < NLOAD; ++i) {
+        x[g][i] = fast_exp2(x[g][i] - mn);
+        ps += x[g][i];
+      }
+      l[g] = fmaf(l[g], alpha, ps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
+    }
+
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+      const int row = i * TPL + rho;
+      uint4 w = vr[i];
+      if (row >= valid) w = make_uint4(0, 0, 0, 0);  // slot past the context: may hold NaN
+      const float v[8] = {Fmt::lo(w.x), Fmt::hi(w.x), Fmt::lo(w.y), Fmt::hi(w.y),
+                          Fmt::lo(w.z), Fmt::hi(w.z), Fmt::lo(w.w), Fmt::hi(w.w)};
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(x[g][i], v[e], acc[g][e]);
+      }
+    }
+  }
+
+  // ---- merge the lane rows of this wave ------------------------------------
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+#pragma unroll
+    for (int off = TPT; off < 64; off <<= 1) {
+      const float mo = shfl_xor(m[g], off);
+      const float lo = shfl_xor(l[g], off);
+      const float mn = fmaxf(m[g], mo);
+      const float f = fast_exp2(m[g] - mn);
+      const float fo = fast_exp2(mo - mn);
+      l[g] = l[g] * f + lo * fo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] = acc[g][e] * f + shfl_xor(acc[g][e], off) * fo;
+      m[g] = mn;
+    }
+  }
+
+  // ---- merge the waves into wave 0 (fixed order: deterministic) ------------
+  __shared__ float mrg_acc[GT][D];
+  __shared__ float mrg_ml[GT][2];
+  for (int w = 1; w < kWaves; ++w) {
+    __syncthreads();
+    if (wave == w && rho == 0) {
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mrg_acc[g][c * 8 + e] = acc[g][e];
+        if (c == 0) {
+          mrg_ml[g][0] = m[g];
+          mrg_ml[g][1] = l[g];
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        const float mo = mrg_ml[g][0];
+        const float lo = mrg_ml[g][1];
+        const float mn = fmaxf(m[g], mo);
+        const float f = fast_exp2(m[g] - mn);
+        const float fo = fast_exp2(mo - mn);
+        l[g] = l[g] * f + lo * fo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = acc[g][e] * f + mrg_acc[g][c * 8 + e] * fo;
+        m[g] = mn;
+      }
+    }
+  }
+
+  // ---- finalise -------------------------------------------------------------
+  if (wave != 0 || rho != 0) return;
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    if (g >= nh) break;
+    const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
+    const size_t row = (size_t)seq * a.num_heads + h0 + g;
+    if (single) {
+      uint4 o;
+      o.x = Fmt::pack(acc[g][0] * inv, acc[g][1] * inv);
+      o.y = Fmt::pack(acc[g][2] * inv, acc[g][3] * inv);
+      o.z = Fmt::pack(acc[g][4] * inv, acc[g][5] * inv);
+      o.w = Fmt::pack(acc[g][6] * inv, acc[g][7] * inv);
+      reinterpret_cast<uint4*>(a.out)[row * CH + c] = o;
+    } else {
+      const size_t slot = row * a.num_partitions + part;
+      float4* o = reinterpret_cast<float4*>(a.ws_o + slot * D + c * 8);
+      o[0] = make_float4(acc[g][0] * inv, acc[g][1] * inv, acc[g][2] * inv, acc[g][3] * inv);
+      o[1] = make_float4(acc[g][4] * inv, acc[g][5] * inv, acc[g][6] * inv, acc[g][7] * inv);
+      if (c == 0) reinterpret_cast<float2*>(a.ws_ml)[slot] = make_float2(m[g], l[g]);
+    }
+  }
+}
+
+namespace {
+
+template <typename Fmt, int D, int GT>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
+  const int nhc = (a.group + GT - 1) / GT;
+  dim3 grid(a.num_kv_heads * nhc, a.num_seqs, a.num_partitions);
+  decode_valu_kernel<Fmt, D, GT><<<grid, kWaves * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename Fmt, int D>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
+  switch (valu_heads_per_workgroup(a.group)) {
+    case 1: return launch_t<Fmt, D, 1>(a, s);
+    case 2: return launch_t<Fmt, D, 2>(a, s);
+    case 4: return launch_t<Fmt, D, 4>(a, s);
+    default: return launch_t<Fmt, D, 8>(a, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, hipStream_t s) {
+  if (dtype == 0) return head_size == 64 ? launch_g<F16, 64>(a, s) : launch_g<F16, 128>(a, s);
+  return head_size == 64 ? launch_g<BF16, 64>(a, s) : launch_g<BF16, 128>(a, s);
+}
+
+}  // namespace pa

@@ -1,0 +1,119 @@
+// Device helpers shared by the gfx950 decode kernels: 16-bit storage formats,
+// DPP cross-lane moves, exp2 and the online-softmax merge.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pa {
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Running-max sentinel.  Finite on purpose: masked scores take this value, so
+// "sentinel - sentinel" is 0, never NaN; a state that only ever saw masked
+// tokens is wiped by the exp2(sentinel - finite) = 0 rescale on the first
+// real token or at the merge.
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- 16-bit storage formats -------------------------------------------------
+
+struct F16 {
+  // value of the low / high half of a packed pair
+  static __device__ __forceinline__ float lo(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+  }
+  // a.x * b.x + a.y * b.y + c, products exact, fp32 accumulate
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  c, false);
+  }
+  // round-to-nearest-even pack of two floats (x in the low half)
+  static __device__ __forceinline__ uint32_t pack(float x, float y) {
+    f16x2_t v = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+struct BF16 {
+  static __device__ __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
+  static __device__ __forceinline__ float hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+  }
+  static __device__ __forceinline__ uint32_t pack(float x, float y) {
+    bf16x2_t v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+// Two 16-bit halves from two words: (lo half of a | lo half of b << 16) etc.
+__device__ __forceinline__ uint32_t pack_lo_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// ---- cross-lane moves ---------------------------------------------------------
+
+// DPP controls (gfx9 encoding)
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;    // lane i <- lane 15-i within a row of 16
+constexpr int kDppRowHalfMirror = 0x141;// lane i <- lane 7-i within each half row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N lanes (N = 8 or 16); every lane of the group
+// receives the group total.  Four (three) DPP-fused adds, no LDS.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  if constexpr (N == 16) x += dpp<kDppRowMirror>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppQuadXor1>(x);
+  return x;
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int mask) {
+  const int lane = threadIdx.x & 63;
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+
+// True if any lane of the wave has `p` set.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// ---- loads --------------------------------------------------------------------
+
+// Streaming loads of K/V: every byte is read exactly once per call, so these
+// are issued with the non-temporal hint (no reuse expected in the caches).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_nt(const uint2* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+}  // namespace pa

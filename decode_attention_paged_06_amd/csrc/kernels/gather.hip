@@ -1,0 +1,57 @@
+// gather_cached_kv: copy the K and V rows of a list of cache slots into
+// contiguous [num_tokens, num_kv_heads, head_size] tensors, bit for bit (the
+// "Memcpy kernel for flash attention" of vLLM PR #29).
+//
+// One thread moves one 16-byte chunk of K and the same chunk of V.  A
+// (token, head) row is head_size * 2 contiguous bytes at both ends, so
+// consecutive threads read and write consecutive 16-byte chunks; a row is
+// never split across a wave boundary for head sizes that divide 64 chunks.
+// Only integer moves: NaN payloads and signed zeros pass through unchanged.
+#include "../launch.h"
+#include "device_common.h"
+
+namespace pa {
+
+__global__ __launch_bounds__(256) void gather_kv_kernel(uint4* __restrict__ k_out,
+                                                         uint4* __restrict__ v_out,
+                                                         const uint4* __restrict__ k_cache,
+                                                         const uint4* __restrict__ v_cache,
+                                                         const int32_t* __restrict__ slots,
+                                                         uint32_t total, uint32_t ch,
+                                                         uint32_t hkv, uint32_t bs) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const uint32_t row = i / ch;          // token * hkv + head
+    const uint32_t c = i - row * ch;
+    const uint32_t tok = row / hkv;
+    const uint32_t head = row - tok * hkv;
+    const int32_t slot = slots[tok];
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (slot >= 0) {
+      const uint32_t blk = (uint32_t)slot / bs;
+      const uint32_t off = (uint32_t)slot - blk * bs;
+      const size_t src = (((size_t)blk * hkv + head) * bs + off) * ch + c;
+      kv = load_nt(k_cache + src);
+      vv = load_nt(v_cache + src);
+    }
+    k_out[i] = kv;
+    v_out[i] = vv;
+  }
+}
+
+hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                         const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, hipStream_t s) {
+  const uint32_t ch = (uint32_t)head_size / 8;
+  const uint32_t total = (uint32_t)num_tokens * (uint32_t)num_kv_heads * ch;
+  const uint32_t threads = 256;
+  uint32_t blocks = (total + threads - 1) / threads;
+  if (blocks > 65536u) blocks = 65536u;
+  gather_kv_kernel<<<blocks, threads, 0, s>>>(
+      static_cast<uint4*>(k_out), static_cast<uint4*>(v_out), static_cast<const uint4*>(k_cache),
+      static_cast<const uint4*>(v_cache), slots, total, ch, (uint32_t)num_kv_heads,
+      (uint32_t)block_size);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,53 @@
+// Internal interface between the C-ABI host layer (host/api.cpp) and the
+// HIP kernels (kernels/*.hip).  Not installed; the public contract is
+// include/paged_attention.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pa {
+
+constexpr int kBlockSize = 16;   // tokens per cache block the decode kernels are built for
+constexpr int kWaves = 4;        // waves per decode workgroup
+constexpr int kMaxGroup = 64;    // largest num_heads / num_kv_heads supported
+
+// Everything a decode launch needs.  Pointers are device memory.
+struct DecodeArgs {
+  void* out;                    // [S, Hq, D] storage type
+  const void* q;                // [S, Hq, D]
+  const void* k_cache;          // [NB, Hkv, BS, D]
+  const void* v_cache;          // [NB, Hkv, BS, D]
+  const int32_t* block_tables;  // [S, MAXB]
+  const int32_t* context_lens;  // [S]
+  const float* alibi;           // [Hq] or nullptr
+  float* ws_o;                  // [S, Hq, P, D] fp32 normalised partial outputs (split only)
+  float* ws_ml;                 // [S, Hq, P, 2] fp32 (running max in log2 units, sum)
+  float scale_log2;             // scale * log2(e)
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int32_t group;                // num_heads / num_kv_heads
+  int32_t num_partitions;       // 1 = single pass straight to `out`
+  int32_t partition_blocks;     // cache blocks per partition
+};
+
+// Query heads per VALU workgroup for a group size (heads that share a kv head
+// are processed in chunks of this many; larger groups use several chunks).
+inline int valu_heads_per_workgroup(int group) {
+  return group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8;
+}
+
+// dtype: 0 = fp16, 1 = bf16 (pa_dtype).  head_size: 64 or 128.
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, hipStream_t s);
+hipError_t launch_partition_reduce(const DecodeArgs& a, int dtype, int head_size, hipStream_t s);
+
+hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                         const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,113 @@
+"""Python binding with the C ABI's names: argument marshalling only.
+
+torch supplies device memory and the current stream; every step of the
+computation runs in the HIP kernels of libpagedattn.so.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (PA_BF16, PA_ENGINE_AUTO, PA_ENGINE_MFMA, PA_ENGINE_VALU, PA_F16, PaDims,
+                   PaOpts, PaPlan, check, lib)
+
+_DTYPE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+_ENGINE = {"auto": PA_ENGINE_AUTO, "valu": PA_ENGINE_VALU, "mfma": PA_ENGINE_MFMA}
+
+
+def make_dims(query: torch.Tensor, key_cache: torch.Tensor, block_tables: torch.Tensor) -> PaDims:
+    S, Hq, D = query.shape
+    NB, Hkv, BS, D2 = key_cache.shape
+    return PaDims(S, Hq, Hkv, D, BS, NB, block_tables.shape[1], _DTYPE[query.dtype])
+
+
+def make_opts(partition_size: int = 0, engine: str = "auto", num_cus: int = 0) -> PaOpts:
+    return PaOpts(int(partition_size), _ENGINE[engine], int(num_cus), 0)
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def paged_attention_plan(dims: PaDims, workspace_bytes: int, opts: Optional[PaOpts] = None) -> PaPlan:
+    plan = PaPlan()
+    check(lib().paged_attention_plan(ctypes.byref(dims), workspace_bytes,
+                                     ctypes.byref(opts) if opts else None, ctypes.byref(plan)))
+    return plan
+
+
+def paged_attention_workspace_bytes(dims: PaDims, opts: Optional[PaOpts] = None) -> int:
+    return int(lib().paged_attention_workspace_bytes(ctypes.byref(dims),
+                                                     ctypes.byref(opts) if opts else None))
+
+
+def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                           value_cache: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, scale: float, block_size: int,
+                           alibi_slopes: Optional[torch.Tensor] = None, stream=None,
+                           workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
+                           engine: str = "auto") -> torch.Tensor:
+    """Enqueue paged decode attention; writes and returns ``out`` ([S, Hq, D]).
+
+    ``workspace`` (uint8 device tensor) is allocated with torch when omitted
+    and the plan needs one.
+    """
+    for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
+                 (value_cache, "value_cache")):
+        _require(t, n, query.dtype)
+    _require(block_tables, "block_tables", torch.int32)
+    _require(context_lens, "context_lens", torch.int32)
+    if alibi_slopes is not None:
+        _require(alibi_slopes, "alibi_slopes", torch.float32)
+    if query.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {query.dtype}")
+    dims = make_dims(query, key_cache, block_tables)
+    opts = make_opts(partition_size, engine)
+    if workspace is None:
+        nbytes = paged_attention_workspace_bytes(dims, opts)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=query.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _require(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().paged_attention_decode(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), int(block_size),
+        alibi_slopes.data_ptr() if alibi_slopes is not None else None, _stream_ptr(stream),
+        ctypes.byref(dims), ws_ptr, ws_bytes, ctypes.byref(opts)))
+    return out
+
+
+def gather_cached_kv(key_out: torch.Tensor, value_out: torch.Tensor, key_cache: torch.Tensor,
+                     value_cache: torch.Tensor, slot_mapping: torch.Tensor, block_size: int,
+                     stream=None):
+    """Enqueue the bit-exact gather of cache rows into key_out/value_out ([T, Hkv, D])."""
+    for t, n in ((key_out, "key_out"), (value_out, "value_out"), (key_cache, "key_cache"),
+                 (value_cache, "value_cache")):
+        _require(t, n, key_cache.dtype)
+    _require(slot_mapping, "slot_mapping", torch.int32)
+    NB, Hkv, BS, D = key_cache.shape
+    check(lib().gather_cached_kv(
+        key_out.data_ptr(), value_out.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        slot_mapping.data_ptr(), slot_mapping.shape[0], Hkv, D, int(block_size), NB,
+        _DTYPE[key_cache.dtype], _stream_ptr(stream)))
+    return key_out, value_out
+
+
+__all__ = ["paged_attention_decode", "paged_attention_plan", "paged_attention_workspace_bytes",
+           "gather_cached_kv", "make_dims", "make_opts", "_lib"]

@@ -1,0 +1,191 @@
+/*
+ * Paged decode attention for AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * One new query token per (sequence, query head) attends over the K/V vectors
+ * of its context, which sit in fixed-size physical cache blocks reached
+ * through a per-sequence block table.  This is the "single query cached KV
+ * attention" operation of vLLM PR #420 ("[OPTIMIZATION] Optimizes the
+ * single_query_cached_kv_attention kernel"), with the MQA/GQA head mapping of
+ * vLLM PR #452 ("Optimize MQA Kernel": head_mapping = repeat_interleave(
+ * arange(num_kv_heads), num_queries_per_kv), num_heads % num_kv_heads == 0),
+ * the optional ALiBi bias switched by use_alibi in the kernel-latency
+ * benchmark of vLLM PR #2744 ("[Performance] Support MQA/GQA in decode phase
+ * by using FlashAttention"), and the split-context variant that the same
+ * page's "Paged attention V2" column times.  gather_cached_kv is the copy of
+ * cached K/V rows into contiguous tensors of vLLM PR #29 ("Memcpy kernel for
+ * flash attention").
+ *
+ * For sequence s with context length L = context_lens[s] and query head h:
+ *
+ *   kvh        = h / (num_heads / num_kv_heads)
+ *   z_t        = scale * dot(query[s,h,:], K_s[kvh, t, :])
+ *                + (alibi_slopes ? alibi_slopes[h] * (t - (L - 1)) : 0)
+ *   out[s,h,:] = sum_t softmax(z)_t * V_s[kvh, t, :],   t = 0 .. L - 1
+ *
+ * where token t of sequence s is row (t % block_size) of physical block
+ * block_tables[s, t / block_size].
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are device memory owned by the caller.  The library
+ *     allocates nothing and keeps no device memory.
+ *   - Tensors are dense and row-major in the layouts stated below.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns without synchronising; outputs are valid once the stream has
+ *     reached that point.  The library never reads device memory on the host.
+ *   - Return value: PA_OK (0) or one of the PA_ERR_* codes.  A non-zero code
+ *     means nothing was enqueued.  pa_last_error() then gives a message for
+ *     the calling thread.  No entry point aborts, throws or exits.
+ *   - Entry points are thread-safe and re-entrant.
+ */
+#ifndef PAGED_ATTENTION_H
+#define PAGED_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Identical to hipStream_t. */
+typedef struct ihipStream_t* pa_stream_t;
+
+/* Storage type of query, caches and output. */
+typedef enum { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Status codes. */
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, bad dimension, inconsistent arguments   */
+  PA_ERR_UNSUPPORTED = 2, /* dtype / head_size / block_size / group size not built */
+  PA_ERR_ALIGNMENT = 3,   /* pointer not aligned as required                        */
+  PA_ERR_WORKSPACE = 4,   /* a forced split needs more workspace than given         */
+  PA_ERR_LAUNCH = 5,      /* the HIP runtime rejected a launch                      */
+  PA_ERR_DEVICE = 6       /* device query failed                                    */
+};
+
+/* Shapes of one decode call.
+ *   query        [num_seqs, num_heads, head_size]                     dtype
+ *   out          [num_seqs, num_heads, head_size]                     dtype
+ *   key_cache    [num_blocks, num_kv_heads, block_size, head_size]    dtype
+ *   value_cache  [num_blocks, num_kv_heads, block_size, head_size]    dtype
+ *   block_tables [num_seqs, max_blocks_per_seq]                       int32
+ *   context_lens [num_seqs]                                           int32
+ *   alibi_slopes [num_heads]                                          float32, or NULL
+ * Supported: head_size 64 or 128; block_size 16; num_heads % num_kv_heads == 0
+ * with num_heads / num_kv_heads <= 64; fp16 or bf16. */
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_size;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t dtype; /* pa_dtype */
+} pa_dims;
+
+/* Which inner engine computes q.K and p.V. */
+typedef enum {
+  PA_ENGINE_AUTO = 0, /* the planner's choice                                         */
+  PA_ENGINE_VALU = 1, /* vector ALU: packed dot products, DPP cross-lane reductions     */
+  PA_ENGINE_MFMA = 2  /* matrix cores: the query group as a 16-wide MFMA tile           */
+} pa_engine;
+
+/* Optional overrides (pass NULL for the defaults). */
+typedef struct {
+  /* 0: the planner decides; -1: force one pass per (sequence, kv head);
+   * > 0: force partitions of this many tokens (a multiple of block_size). */
+  int32_t partition_size;
+  int32_t engine;  /* pa_engine */
+  int32_t num_cus; /* 0: query the current device; > 0: plan for this many CUs */
+  int32_t reserved;
+} pa_opts;
+
+/* A launch plan (output of paged_attention_plan). */
+typedef struct {
+  int32_t num_partitions; /* partitions per sequence; 1 = single pass, no reduce  */
+  int32_t partition_size; /* tokens per partition (multiple of block_size)         */
+  int32_t engine;         /* resolved pa_engine                                     */
+  int32_t reserved;
+  size_t workspace_bytes; /* workspace this plan uses (0 for a single pass)         */
+} pa_plan;
+
+/*
+ * paged_attention_decode -- decode attention over a paged KV cache.
+ *
+ * out, query, key_cache, value_cache, block_tables, context_lens: see pa_dims.
+ *   out, query, key_cache and value_cache must be 16-byte aligned,
+ *   block_tables and context_lens 4-byte aligned.
+ * scale        multiplies q.k (callers normally pass 1/sqrt(head_size)).
+ * block_size   must equal dims->block_size.
+ * alibi_slopes one fp32 slope per query head, or NULL for no bias.
+ * stream       HIP stream the kernels are enqueued on.
+ * dims         shapes (host memory).
+ * workspace    device scratch for the split-context partials, 256-byte
+ *              aligned, or NULL when workspace_bytes is 0.  Size it with
+ *              paged_attention_workspace_bytes().  Contents on entry are
+ *              ignored; the call owns it until the stream passes the call.
+ * opts         NULL, or overrides (host memory).
+ *
+ * Device-side preconditions (not checked, as that would need a host read):
+ *   block ids in block_tables[s, 0 .. ceil(L/block_size) - 1] lie in
+ *   [0, num_blocks); 0 <= L <= max_blocks_per_seq * block_size (larger values
+ *   are clamped to that bound).  Table entries past a sequence's last block
+ *   and cache slots past L in its last block are never used and may hold
+ *   anything, NaN included.  A sequence with L = 0 gets a zero output row.
+ *
+ * With opts == NULL an undersized workspace makes the planner use fewer
+ * partitions (down to a single pass); it never fails for lack of workspace.
+ */
+int paged_attention_decode(void* out, const void* query, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, float scale, int32_t block_size,
+                           const float* alibi_slopes, pa_stream_t stream, const pa_dims* dims,
+                           void* workspace, size_t workspace_bytes, const pa_opts* opts);
+
+/*
+ * paged_attention_workspace_bytes -- workspace the planner's choice needs for
+ * these shapes and overrides when given unlimited workspace (0 if it picks a
+ * single pass).  Host only; returns 0 for invalid dims.
+ */
+size_t paged_attention_workspace_bytes(const pa_dims* dims, const pa_opts* opts);
+
+/*
+ * paged_attention_plan -- the launch plan paged_attention_decode would use
+ * with this much workspace.  Host only: it touches no device unless
+ * opts->num_cus is 0, in which case it queries the current device's compute
+ * unit count once.  Returns a status code; *plan is written on PA_OK.
+ */
+int paged_attention_plan(const pa_dims* dims, size_t workspace_bytes, const pa_opts* opts,
+                         pa_plan* plan);
+
+/*
+ * gather_cached_kv -- copy cached K/V rows into contiguous tensors, bit for
+ * bit (the operation benchmarked on vLLM PR #29, whose parameters are
+ * num_tokens, num_heads, head_size, block_size and num_blocks).
+ *
+ * key_out, value_out  [num_tokens, num_kv_heads, head_size]            dtype
+ * key_cache, value_cache [num_blocks, num_kv_heads, block_size, head_size] dtype
+ * slot_mapping        [num_tokens] int32; slot = block * block_size + offset.
+ *                     A negative slot writes a zero row.  Slots must be
+ *                     < num_blocks * block_size (device-side precondition).
+ * head_size must be a multiple of 8; pointers to 16-bit data 16-byte aligned.
+ * Any block_size >= 1 is accepted.
+ */
+int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
+                     const void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                     int32_t num_blocks, int32_t dtype, pa_stream_t stream);
+
+/* Static description of a status code. */
+const char* pa_status_string(int status);
+
+/* Message for the calling thread's most recent non-zero status ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_H */

@@ -1,0 +1,86 @@
+"""Helpers for the GPU parity tests: run the HIP path, run the oracle, compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from decode_attention_paged_06_amd import paged_attention_decode
+from workloads import decode_inputs, raw_u16
+
+# Max-abs tolerances against the fp64 oracle: fp16 2e-3, bf16 1e-2.
+TOL = {"f16": 2e-3, "bf16": 1e-2}
+
+
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def make(device_="cpu", **kw):
+    return decode_inputs(device=device_, **kw)
+
+
+def to_device(inp, dev):
+    for k in ("query", "key_cache", "value_cache", "block_tables", "context_lens", "alibi_slopes"):
+        t = getattr(inp, k)
+        if t is not None:
+            setattr(inp, k, t.to(dev))
+    return inp
+
+
+def run(inp, engine="auto", partition_size=0, out=None):
+    if out is None:
+        out = torch.full_like(inp.query, float("nan"))
+    paged_attention_decode(out, inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
+                           inp.context_lens, inp.scale, inp.block_size, inp.alibi_slopes,
+                           partition_size=partition_size, engine=engine)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_ref(inp, seqs=None):
+    """Oracle output for `seqs` (all by default), copying only their blocks to the host."""
+    S = inp.query.shape[0]
+    seqs = list(range(S)) if seqs is None else list(seqs)
+    BS = inp.block_size
+    lens = inp.context_lens.cpu().numpy()
+    tables = inp.block_tables.cpu().numpy()
+    maxb = tables.shape[1]
+    # compact pool: the used blocks of the sampled sequences, in table order
+    phys, rows = [], []
+    for s in seqs:
+        L = min(int(lens[s]), maxb * BS)
+        nb = (L + BS - 1) // BS if L > 0 else 0
+        rows.append(list(range(len(phys), len(phys) + nb)) + [0] * (maxb - nb))
+        phys.extend(int(x) for x in tables[s, :nb])
+    if not phys:
+        phys = [0]
+    idx = torch.tensor(phys, dtype=torch.long, device=inp.key_cache.device)
+    kc = raw_u16(inp.key_cache.index_select(0, idx))
+    vc = raw_u16(inp.value_cache.index_select(0, idx))
+    q = raw_u16(inp.query.index_select(0, torch.tensor(seqs, device=inp.query.device)))
+    lens_s = np.minimum(lens[seqs], maxb * BS)
+    slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.cpu().numpy()
+    return oracle.paged_decode(q, kc, vc, np.array(rows), lens_s, inp.scale, BS, slopes,
+                               dtype=inp.dtype)
+
+
+def compare(got: torch.Tensor, ref: np.ndarray, dtype: str, seqs=None, what=""):
+    g = got.float().cpu().numpy()
+    if seqs is not None:
+        g = g[list(seqs)]
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = float(np.max(np.abs(g - ref))) if g.size else 0.0
+    rel = float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)) if g.size else 0.0
+    print(f"  {what}: max_abs={err:.3e} rel_l2={rel:.3e}", flush=True)
+    assert err <= TOL[dtype], f"{what}: max abs error {err} > {TOL[dtype]}"
+    return err, rel
+
+
+def sample_seqs(S, k=16, seed=0):
+    if S <= k:
+        return list(range(S))
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, S - 1), size=k - 2, replace=False)
+    return [0] + sorted(int(x) for x in mid) + [S - 1]

@@ -1,0 +1,202 @@
+"""GPU parity: the HIP decode path against the fp64 oracle.
+
+Tolerance (max abs, per element): 2e-3 for fp16, 1e-2 for bf16.  Integer
+facts (context length 1 returns V, relabelled blocks, determinism) are
+checked bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TOL, compare, device, make, oracle_ref, run, sample_seqs, to_device
+from workloads import WORKLOADS, raw_u16, workload_args
+
+pytestmark = pytest.mark.gpu
+
+ENGINES = ["valu", "mfma"]
+
+
+# ---------------------------------------------------------------------------
+# The named workloads at their full sizes, in the auto launch configuration
+# (the one the bench times) and with each engine forced.  Sequences beyond 16
+# are checked on a seeded sample, always including the first and the last.
+# ---------------------------------------------------------------------------
+
+WORKLOAD_CASES = [(name, b) for name, w in WORKLOADS.items() for b in w["batches"]]
+
+
+@pytest.mark.parametrize("name,batch", WORKLOAD_CASES, ids=[f"{n}-b{b}" for n, b in WORKLOAD_CASES])
+def test_workload_parity(name, batch):
+    dev = device()
+    args = workload_args(name, batch)
+    inp = make(device_=dev, poison=True, **args)
+    seqs = sample_seqs(batch, 16, seed=batch)
+    ref = oracle_ref(inp, seqs)
+    for engine in ["auto"] + ENGINES:
+        out = run(inp, engine=engine)
+        compare(out, ref, inp.dtype, seqs, what=f"{name} b={batch} engine={engine}")
+
+
+# ---------------------------------------------------------------------------
+# Split-context partitions: boundaries, ragged tails, every engine and dtype
+# ---------------------------------------------------------------------------
+
+BOUNDARY_LENS = [1, 15, 16, 17, 47, 48, 63, 64, 65, 127, 128, 129, 200, 511, 513, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("alibi", [False, True])
+def test_partitions(dtype, engine, alibi):
+    dev = device()
+    inp = to_device(make(num_seqs=len(BOUNDARY_LENS), num_heads=16, num_kv_heads=2, head_size=128,
+                         block_size=16, dtype=dtype, seed=77, context_lens=BOUNDARY_LENS,
+                         alibi=alibi, poison=True), dev)
+    ref = oracle_ref(inp)
+    for ps in (-1, 0, 16, 32, 48, 64, 256):
+        out = run(inp, engine=engine, partition_size=ps)
+        compare(out, ref, dtype, what=f"{dtype} {engine} alibi={alibi} partition={ps}")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("group", [1, 2, 3, 8, 16, 20, 48, 64])
+def test_group_sizes(engine, group):
+    dev = device()
+    Hkv = 2 if group <= 16 else 1
+    inp = to_device(make(num_seqs=3, num_heads=group * Hkv, num_kv_heads=Hkv, head_size=128,
+                         block_size=16, dtype="bf16", seed=100 + group, context_lens=[5, 130, 77],
+                         alibi=True, poison=True), dev)
+    ref = oracle_ref(inp)
+    for ps in (-1, 64):
+        compare(run(inp, engine=engine, partition_size=ps), ref, "bf16",
+                what=f"G={group} {engine} partition={ps}")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("head_size", [64, 128])
+def test_head_sizes_fp16(engine, head_size):
+    dev = device()
+    inp = to_device(make(num_seqs=5, num_heads=8, num_kv_heads=4, head_size=head_size,
+                         block_size=16, dtype="f16", seed=9, context_lens=[1, 2, 33, 64, 250],
+                         poison=True), dev)
+    ref = oracle_ref(inp)
+    for ps in (-1, 32):
+        compare(run(inp, engine=engine, partition_size=ps), ref, "f16",
+                what=f"D={head_size} {engine} partition={ps}")
+
+
+# ---------------------------------------------------------------------------
+# Closed forms, invariants and edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_context_one_returns_v_exactly(engine, dtype):
+    dev = device()
+    inp = to_device(make(num_seqs=6, num_heads=16, num_kv_heads=4, head_size=128, block_size=16,
+                         dtype=dtype, seed=3, context_lens=1, alibi=True, poison=True,
+                         max_blocks_per_seq=8), dev)
+    vc = raw_u16(inp.value_cache)
+    tables = inp.block_tables.cpu().numpy()
+    for ps in (-1, 16):
+        got = raw_u16(run(inp, engine=engine, partition_size=ps))
+        for s in range(6):
+            for h in range(16):
+                assert np.array_equal(got[s, h], vc[tables[s, 0], h // 4, 0]), (s, h, ps)
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_empty_context_gives_zeros(engine):
+    dev = device()
+    inp = to_device(make(num_seqs=4, num_heads=8, num_kv_heads=1, head_size=128, block_size=16,
+                         dtype="bf16", seed=4, context_lens=[0, 20, 0, 3], poison=True,
+                         max_blocks_per_seq=4), dev)
+    ref = oracle_ref(inp)
+    for ps in (-1, 16):
+        out = run(inp, engine=engine, partition_size=ps)
+        assert not out[0].float().abs().sum().item() and not out[2].float().abs().sum().item()
+        compare(out, ref, "bf16", what=f"empty {engine} partition={ps}")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_deterministic_and_block_relabelling(engine):
+    dev = device()
+    inp = to_device(make(num_seqs=5, num_heads=32, num_kv_heads=4, head_size=128, block_size=16,
+                         dtype="bf16", seed=12, context_lens=[300, 17, 1024, 64, 555],
+                         alibi=True), dev)
+    for ps in (-1, 128):
+        a = raw_u16(run(inp, engine=engine, partition_size=ps))
+        b = raw_u16(run(inp, engine=engine, partition_size=ps))
+        assert np.array_equal(a, b), "two identical calls differ"
+        # move every physical block to a new id: same bytes, same order of work
+        NB = inp.key_cache.shape[0]
+        pi = torch.randperm(NB, generator=torch.Generator().manual_seed(1)).to(dev)
+        kc = torch.empty_like(inp.key_cache)
+        vc = torch.empty_like(inp.value_cache)
+        kc[pi] = inp.key_cache
+        vc[pi] = inp.value_cache
+        moved = make(num_seqs=1, num_heads=1, num_kv_heads=1, head_size=128, block_size=16,
+                     dtype="bf16", seed=0, context_lens=1)
+        moved.query, moved.key_cache, moved.value_cache = inp.query, kc, vc
+        moved.block_tables = pi[inp.block_tables.long()].to(torch.int32).contiguous()
+        moved.context_lens, moved.alibi_slopes, moved.scale = inp.context_lens, inp.alibi_slopes, inp.scale
+        c = raw_u16(run(moved, engine=engine, partition_size=ps))
+        assert np.array_equal(a, c), "relabelled blocks changed the result"
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_needle(engine):
+    """q = c K[t*] puts all softmax weight on t*: out = V[t*] up to rounding."""
+    dev = device()
+    lens = [40, 300]
+    inp = make(num_seqs=2, num_heads=8, num_kv_heads=1, head_size=128, block_size=16,
+               dtype="f16", seed=21, context_lens=lens, poison=True)
+    kc = inp.key_cache.float()
+    tables = inp.block_tables
+    for tstar in (0, 15, 16, 17, 39):
+        for s in range(2):
+            t = tstar if s == 0 else 255 - tstar
+            k = kc[tables[s, t // 16], 0, t % 16]
+            # 8 heads: 8 different needle strengths, all large
+            for h in range(8):
+                inp.query[s, h] = (k * (0.5 + 0.1 * h)).to(torch.float16)
+        g = to_device(make(num_seqs=2, num_heads=8, num_kv_heads=1, head_size=128, block_size=16,
+                           dtype="f16", seed=21, context_lens=lens, poison=True), dev)
+        g.query = inp.query.to(dev)
+        ref = oracle_ref(g)
+        for ps in (-1, 32):
+            compare(run(g, engine=engine, partition_size=ps), ref, "f16",
+                    what=f"needle t*={tstar} {engine} partition={ps}")
+
+
+def test_gqa_equals_repeated_mha():
+    dev = device()
+    G = 8
+    gqa = to_device(make(num_seqs=3, num_heads=16, num_kv_heads=2, head_size=128, block_size=16,
+                         dtype="bf16", seed=31, context_lens=[100, 7, 400], alibi=True), dev)
+    mha = to_device(make(num_seqs=3, num_heads=16, num_kv_heads=2, head_size=128, block_size=16,
+                         dtype="bf16", seed=31, context_lens=[100, 7, 400], alibi=True), dev)
+    mha.key_cache = gqa.key_cache.repeat_interleave(G, dim=1).contiguous()
+    mha.value_cache = gqa.value_cache.repeat_interleave(G, dim=1).contiguous()
+    ref = oracle_ref(gqa)
+    for engine in ENGINES:
+        a = run(gqa, engine=engine)
+        b = run(mha, engine=engine)
+        compare(a, ref, "bf16", what=f"gqa {engine}")
+        compare(b, ref, "bf16", what=f"repeated mha {engine}")
+        assert float((a.float() - b.float()).abs().max()) <= TOL["bf16"]
+
+
+def test_stream_argument_is_used():
+    dev = device()
+    inp = to_device(make(num_seqs=2, num_heads=8, num_kv_heads=2, head_size=128, block_size=16,
+                         dtype="bf16", seed=41, context_lens=[500, 900]), dev)
+    ref = oracle_ref(inp)
+    s = torch.cuda.Stream()
+    out = torch.empty_like(inp.query)
+    from decode_attention_paged_06_amd import paged_attention_decode
+    with torch.cuda.stream(s):
+        paged_attention_decode(out, inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
+                               inp.context_lens, inp.scale, 16, None, stream=s, partition_size=64)
+    s.synchronize()
+    compare(out, ref, "bf16", what="side stream")

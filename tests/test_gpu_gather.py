@@ -1,0 +1,40 @@
+"""GPU parity of gather_cached_kv: bit-exact against the oracle's raw copy."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_paged_06_amd import gather_cached_kv
+from gpu_util import device
+from workloads import gather_inputs, raw_u16
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # tokens, kv heads, head size, block size, blocks, dtype, negative slots
+    (64, 40, 128, 8, 1024, "f16", 0),     # the gather benchmark's shape, smallest batch
+    (2048, 40, 128, 8, 1024, "f16", 0),   # ... and its largest
+    (1000, 8, 128, 16, 4096, "bf16", 7),
+    (333, 1, 64, 16, 64, "f16", 3),
+    (17, 3, 8, 5, 11, "bf16", 2),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"T{c[0]}-H{c[1]}-D{c[2]}-BS{c[3]}" for c in CASES])
+@pytest.mark.parametrize("random_bits", [False, True])
+def test_gather_bit_exact(case, random_bits):
+    dev = device()
+    T, H, D, BS, NB, dtype, neg = case
+    g = gather_inputs(num_tokens=T, num_kv_heads=H, head_size=D, block_size=BS, num_blocks=NB,
+                      dtype=dtype, seed=T + H, random_bits=random_bits, num_negative=neg,
+                      device=dev)
+    ko = torch.empty((T, H, D), dtype=g.key_cache.dtype, device=dev)
+    vo = torch.empty_like(ko)
+    ko.view(torch.int16).fill_(0x5555)   # the kernel must overwrite every row
+    vo.view(torch.int16).fill_(0x5555)
+    gather_cached_kv(ko, vo, g.key_cache, g.value_cache, g.slot_mapping, BS)
+    torch.cuda.synchronize()
+    rk, rv = oracle.gather_cached_kv(raw_u16(g.key_cache), raw_u16(g.value_cache),
+                                     g.slot_mapping.cpu().numpy(), BS)
+    assert np.array_equal(raw_u16(ko), rk)
+    assert np.array_equal(raw_u16(vo), rv)
