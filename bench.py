@@ -47,7 +47,60 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the calls replayed from a HIP graph (GPU time without the "
+                         "host launch path; matters for small, launch-bound batches)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of decoding, run --steps device-to-device copies of MIB MiB "
+                         "(reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib, steps):
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n,
+                      "bytes_written_per_copy": n, "copies": steps}), flush=True)
+
+
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def recorded_traffic(kernel: str, workload: str, batch: int):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, or None.
+
+    A summary under profiles/ ends with a JSON record of the scaled
+    FETCH_SIZE + WRITE_SIZE traffic and a SHA-256 of the kernel's sources at
+    the time the counters were taken; the figure is used only while the
+    sources still hash the same.
+    """
+    import glob
+    import hashlib
+
+    for path in sorted(glob.glob(os.path.join(PROFILE_DIR, "*.md"))):
+        text = open(path).read()
+        for line in text.splitlines():
+            if not line.startswith('{"kernel"'):
+                continue
+            rec = json.loads(line)
+            if (kernel not in rec["kernel"] or rec["workload"] != workload
+                    or rec["batch"] != batch):
+                continue
+            h = hashlib.sha256()
+            try:
+                for f in rec["sources"]:
+                    h.update(open(os.path.join(ROOT, f), "rb").read())
+            except OSError:
+                return None
+            if h.hexdigest() == rec["sources_sha256"]:
+                return rec["traffic_bytes_per_launch"]
+    return None
 
 
 def workload_label(name, args):
@@ -100,6 +153,9 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); the decode "
               "kernel has no cross-GPU path to measure", file=sys.stderr)
         sys.exit(2)
+    if a.calibrate_copy:
+        calibrate_copy(a.calibrate_copy, a.steps)
+        return
 
     import torch
 
@@ -126,7 +182,8 @@ def main():
     sets = [first]
     for i in range(1, nsets):
         # same lengths and shapes, fresh values and block assignment
-        sets.append(decode_inputs(device=dev, **dict(args, seed=args["seed"] + 100000 * i)))
+        sets.append(decode_inputs(device=dev, **dict(args, seed=args["seed"] + 100000 * i,
+                                                      context_lens=lens)))
     outs = [torch.empty_like(s.query) for s in sets]
 
     dims = make_dims(first.query, first.key_cache, first.block_tables)
@@ -168,6 +225,36 @@ def main():
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
 
+    graph_us = None
+    if a.graph:
+        # Capture one rotation of calls (at least 20) into a graph and replay it:
+        # the GPU then runs the kernels back to back, so the time is the
+        # device time of the calls without the host launch path.
+        ncap = max(20, nsets)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(ncap):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(ncap):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, a.steps // ncap)
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) * 1e3 / (reps * ncap)
+
+    kernel_name = "decode_mfma_kernel" if plan.engine == 2 else "decode_valu_kernel"
     context = PAGES_US.get((name, batch))
     vs = None
     if context:
@@ -204,8 +291,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
-            "kernel": "decode_mfma_kernel" if plan.engine == 2 else "decode_valu_kernel",
+            "traffic": recorded_traffic(kernel_name, name, batch),
+            "kernel": kernel_name,
             "kernel_avg_us": round(avg_ms * 1e3, 2),
             "flops_per_call": flops,
             "note": ("per-call HIP events on the launch stream; one decode kernel per call"
@@ -214,6 +301,11 @@ def main():
         },
         "wall_s_timed_region": round(wall, 3),
     }
+    if graph_us is not None:
+        result["graph_replay"] = {"us_per_call": round(graph_us, 3),
+                                  "GB/s": round(nbytes / (graph_us * 1e-6) / 1e9, 2),
+                                  "pct_of_hbm_peak": round(100 * nbytes / (graph_us * 1e-6) / 1e9
+                                                           / HBM_PEAK_GBPS, 2)}
     if context:
         result["pages_context"] = dict(context, note="A100 numbers from the reference pages; "
                                        "vs_baseline = FlashAttention A100 us / this us")

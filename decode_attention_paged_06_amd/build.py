@@ -29,7 +29,7 @@ SOURCES = [
 ]
 
 ARCH = "gfx950"
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}"]
 # Packed-fp32 VALU forms are disabled for all device code.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
@@ -41,12 +41,12 @@ def _hipcc() -> str:
     return path
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, src.replace("/", "_") + ".o")
-    cmd = [_hipcc()] + COMMON
+def _compile(src: str, csrc: str = CSRC, build_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(build_dir, src.replace("/", "_") + ".o")
+    cmd = [_hipcc()] + COMMON + [f"-I{csrc}"]
     if src.endswith(".hip"):
         cmd += DEVICE + ["-x", "hip"]
-    cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd += ["-c", os.path.join(csrc, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32 feature
     err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
@@ -57,20 +57,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = True, csrc: str = CSRC, out: str = LIB_PATH) -> str:
+    """Compile `csrc` (default: this package's sources) into the shared library `out`."""
+    build_dir = BUILD_DIR if csrc == CSRC else os.path.join(os.path.dirname(out), "_build")
+    os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, csrc, build_dir), SOURCES))
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
-    build()
+    import argparse
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--csrc", default=CSRC, help="source tree (default: this package's csrc/)")
+    ap.add_argument("--out", default=LIB_PATH, help="output shared library")
+    ns = ap.parse_args()
+    build(csrc=os.path.abspath(ns.csrc), out=os.path.abspath(ns.out))

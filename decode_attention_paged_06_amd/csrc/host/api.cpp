@@ -130,6 +130,7 @@ int make_plan(const pa_dims* d, size_t ws_bytes, const pa_opts* o, bool unlimite
     if (cus < 0) return fail(PA_ERR_INVALID_ARG, "num_cus = %d", cus);
     if (cus == 0 && (st = current_num_cus(&cus))) return st;
     const int group = d->num_heads / d->num_kv_heads;
+    // workgroups per (sequence, kv head): query-head chunks on the VALU path, one on MFMA
     const long long chunks =
         engine == PA_ENGINE_VALU
             ? (group + pa::valu_heads_per_workgroup(group) - 1) / pa::valu_heads_per_workgroup(group)

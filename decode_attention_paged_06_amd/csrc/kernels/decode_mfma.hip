@@ -1,13 +1,23 @@
 // Paged decode attention on the gfx950 matrix cores.
 //
-// Same operation and the same workgroup decomposition as decode_valu.hip
-// (workgroup = kv head x sequence x partition, 4 waves striding over the
-// partition's 16-token cache blocks), but the G query heads that share a kv
-// head are packed as the N = 16 columns of an MFMA tile (HT tiles for G > 16),
-// so each 16-token block is one M = 16 tile:
+// Operation: for one new query token per head, softmax(scale * q.K + alibi).V
+// over the sequence's cached tokens, reached through its block table ("single
+// query cached KV attention", vLLM PR #420; GQA head mapping of vLLM PR #452).
+//
+// Decomposition.  A workgroup (4 waves) owns the query heads that share one
+// kv head (the GQA group, padded to HT tiles of 16 heads), for one sequence
+// and one context partition.  A head tile is the N = 16 side of the MFMA
+// products and each 16-token cache block is one M = 16 tile:
 //
 //   S^T[t, g]   = sum_d K[t, d] q[g, d]    v_mfma_f32_16x16x32_{f16,bf16}, D/32 steps
 //   O^T[d, g]  += sum_t V[t, d] P[g, t]     v_mfma_f32_16x16x16_{f16,bf16}, D/16 tiles
+//
+// Wave w walks the partition's blocks w, w+4, w+8, ... with a two-deep
+// software pipeline (the next block's K/V loads are in flight while the current
+// block is processed); the four waves' softmax states are merged at the end.
+// Every K/V byte is loaded once per workgroup and feeds all HT head tiles;
+// groups of up to 16 heads (HT = 1) keep their q operands in registers,
+// larger groups re-read them from LDS to save registers.
 //
 // Register layouts (lane = 16 j + r, r = lane % 16, j = lane / 16):
 //   K operand, step i : lane holds K[t = r][16-byte chunk 4i + j]; the load for
@@ -23,9 +33,9 @@
 //   output tile m     : lane holds O^T[d = EPL (4j + v) + m][g = r], so lane
 //                       (r, j) owns the contiguous output slice
 //                       d in [4 EPL j, 4 EPL (j + 1)) of head r.
-// The contraction index is free to be any permutation as long as both
-// operands agree, which is what makes these layouts line up with coalesced
-// loads without LDS staging.
+// The contraction index may be any permutation as long as both operands agree,
+// which is what lines these layouts up with coalesced loads and no LDS
+// staging of K or V.
 //
 // Softmax: fp32 online softmax in log2 units; the running max of a head is
 // shared by the 4 lane groups j (two swizzles per block), each lane keeps a
@@ -95,7 +105,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(const DecodeAr
   constexpr float kLog2e = 1.4426950408889634f;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int r = lane & 15;
   const int j = lane >> 4;
 
@@ -115,7 +125,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(const DecodeAr
     }
     return;
   }
-  if (tok0 >= L) return;
+  if (tok0 >= L) return;  // partition past this sequence's end: nothing to do
   const int tok1 = min(L, tok0 + a.partition_blocks * BS);
   const int blk0 = tok0 / BS;
   const int nblk = (tok1 - tok0 + BS - 1) / BS;
@@ -128,12 +138,15 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(const DecodeAr
       q_lds[i] = (i < G * CH) ? qg[i] : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
-  uint4 qb[HT][NK];
+  constexpr bool kQInRegs = HT == 1;
+  uint4 qb[kQInRegs ? NK : 1];
+  if constexpr (kQInRegs) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) qb[i] = q_lds[r * CH + 4 * i + j];
+  }
   float slope[HT];
 #pragma unroll
   for (int n = 0; n < HT; ++n) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) qb[n][i] = q_lds[(n * 16 + r) * CH + 4 * i + j];
     const int g = n * 16 + r;
     slope[n] = (a.alibi != nullptr && g < G) ? a.alibi[h0 + g] * kLog2e : 0.f;
   }
@@ -149,36 +162,48 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(const DecodeAr
   }
 
   const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq + blk0;
-  const size_t bstride = (size_t)a.num_kv_heads * BS * D;  // elements per physical block
-  const size_t head_off = (size_t)kvh * BS * D;
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k_cache) + head_off;
-  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v_cache) + head_off;
-  const int k_lane = r * D + j * 8;        // element offset of this lane's step-0 K chunk
-  const int v_lane = (4 * j) * D + r * EPL;  // element offset of this lane's load-0 V slice
+  // Byte addressing: a wave-uniform block base (SGPRs) plus a small unsigned
+  // per-lane offset, so every K/V load is one buffer load with a VGPR offset.
+  const size_t bstride = (size_t)a.num_kv_heads * BS * D * 2;  // bytes per physical block
+  const size_t head_off = (size_t)kvh * BS * D * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
+  const uint32_t k_lane = (uint32_t)(r * D + j * 8) * 2u;          // step-0 K chunk
+  const uint32_t v_lane = (uint32_t)((4 * j) * D + r * EPL) * 2u;  // load-0 V slice
   const int qpos = L - 1;
 
-  for (int b = wave; b < nblk; b += kWaves) {
-    const int phys = table[b];
-    const uint16_t* kp = kbase + (size_t)phys * bstride + k_lane;
-    const uint16_t* vp = vbase + (size_t)phys * bstride + v_lane;
-    uint4 kr[NK];
-    VT vr[4];
+  // One cache block's K and V in registers.
+  struct Tile {
+    uint4 k[NK];
+    VT v[4];
+  };
+  auto load = [&](Tile& T, int b) {
+    const size_t boff = (size_t)table[b] * bstride;
+    const rsrc_t rk = make_rsrc(kbase + boff, BS * D * 2);
+    const rsrc_t rv = make_rsrc(vbase + boff, BS * D * 2);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kr[i] = load_nt(reinterpret_cast<const uint4*>(kp + i * 32));
+    for (int i = 0; i < NK; ++i) T.k[i] = buffer_load(rk, k_lane + 64u * i, (uint4*)nullptr);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vr[i] = load_nt(reinterpret_cast<const VT*>(vp + i * D));
+    for (int i = 0; i < 4; ++i) T.v[i] = buffer_load(rv, v_lane + 2u * D * i, (VT*)nullptr);
+  };
 
+  auto process = [&](Tile& T, int b) {
     const int tb = (blk0 + b) * BS;
     const int valid = tok1 - tb;
     uint2 pk[HT];
-    bool rescale = false;
     float alpha[HT];
+    bool rescale = false;
 
 #pragma unroll
     for (int n = 0; n < HT; ++n) {
       f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < NK; ++i) s = Mfma<Fmt>::qk(kr[i], qb[n][i], s);
+      for (int i = 0; i < NK; ++i) {
+        uint4 qv;
+        if constexpr (kQInRegs) qv = qb[i];
+        else qv = q_lds[(n * 16 + r) * CH + 4 * i + j];
+        s = Mfma<Fmt>::qk(T.k[i], qv, s);
+      }
       float x[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -210,19 +235,35 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(const DecodeAr
     if (valid < BS) {  // last block of a sequence: slots past L may hold NaN
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (4 * j + i >= valid) vr[i] = VR::zero();
+        if (4 * j + i >= valid) T.v[i] = VR::zero();
     }
 
 #pragma unroll
     for (int t = 0; t < EPL; ++t) {
       const int w = t >> 1;
-      const uint32_t a0 = VR::word(vr[0], w), a1 = VR::word(vr[1], w);
-      const uint32_t a2 = VR::word(vr[2], w), a3 = VR::word(vr[3], w);
+      const uint32_t a0 = VR::word(T.v[0], w), a1 = VR::word(T.v[1], w);
+      const uint32_t a2 = VR::word(T.v[2], w), a3 = VR::word(T.v[3], w);
       const uint2 vt = (t & 1) ? make_uint2(pack_hi_hi(a0, a1), pack_hi_hi(a2, a3))
                                : make_uint2(pack_lo_lo(a0, a1), pack_lo_lo(a2, a3));
 #pragma unroll
       for (int n = 0; n < HT; ++n) acc[n][t] = Mfma<Fmt>::pv(vt, pk[n], acc[n][t]);
     }
+  };
+
+  // Software pipeline: the loads of the wave's next block are in flight while
+  // the current block is processed (two register tiles, used alternately).
+  Tile ta, tb2;
+  int b = wave;
+  if (b < nblk) load(ta, b);
+  while (b < nblk) {
+    const int b1 = b + kWaves;
+    if (b1 < nblk) load(tb2, b1);
+    process(ta, b);
+    if (b1 >= nblk) break;
+    const int b2 = b1 + kWaves;
+    if (b2 < nblk) load(ta, b2);
+    process(tb2, b1);
+    b = b2;
   }
 
   // ---- complete the per-lane sums over the 4 lane groups -------------------
@@ -311,10 +352,12 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
 
 template <typename Fmt, int D>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  if (a.group <= 16) return launch_t<Fmt, D, 1>(a, s);
-  if (a.group <= 32) return launch_t<Fmt, D, 2>(a, s);
-  if (a.group <= 48) return launch_t<Fmt, D, 3>(a, s);
-  return launch_t<Fmt, D, 4>(a, s);
+  switch ((a.group + 15) / 16) {
+    case 1: return launch_t<Fmt, D, 1>(a, s);
+    case 2: return launch_t<Fmt, D, 2>(a, s);
+    case 3: return launch_t<Fmt, D, 3>(a, s);
+    default: return launch_t<Fmt, D, 4>(a, s);
+  }
 }
 
 }  // namespace

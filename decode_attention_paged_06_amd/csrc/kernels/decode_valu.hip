@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
   constexpr float kLog2e = 1.4426950408889634f;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int rho = lane / TPT;   // token row of this lane within a load
   const int c = lane % TPT;     // 16-byte chunk of the row
 

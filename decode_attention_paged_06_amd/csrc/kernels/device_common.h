@@ -116,4 +116,22 @@ __device__ __forceinline__ uint2 load_nt(const uint2* p) {
   return make_uint2(v.x, v.y);
 }
 
+// Buffer resource (V#) over `bytes` bytes at a wave-uniform `base`: loads
+// through it take the base from SGPRs and a 32-bit per-lane byte offset from
+// one VGPR, and return zero (instead of faulting) past `bytes`.  Word 3 is the
+// gfx9 raw-buffer configuration.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+constexpr int kCacheStream = 2;  // "nt": streaming access, no reuse expected
+__device__ __forceinline__ uint4 buffer_load(rsrc_t r, uint32_t off, uint4*) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCacheStream);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 buffer_load(rsrc_t r, uint32_t off, uint2*) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCacheStream);
+  return make_uint2(v.x, v.y);
+}
+
 }  // namespace pa
