@@ -128,22 +128,24 @@ def cpu_baseline(args, budget_s):
     q, kc, vc = raw_u16(inp.query), raw_u16(inp.key_cache), raw_u16(inp.value_cache)
     tables, lens = inp.block_tables.numpy(), inp.context_lens.numpy()
     slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.numpy()
+    # cycle over the sampled sequences until the time budget is spent
     done = []
     t0 = time.perf_counter()
-    for s in range(n):
-        oracle.paged_decode(q, kc, vc, tables, lens, inp.scale, inp.block_size, slopes,
-                            dtype=inp.dtype, seqs=[s])
-        done.append(s)
-        if time.perf_counter() - t0 > budget_s:
-            break
+    while time.perf_counter() - t0 < budget_s:
+        for s in range(n):
+            oracle.paged_decode(q, kc, vc, tables, lens, inp.scale, inp.block_size, slopes,
+                                dtype=inp.dtype, seqs=[s])
+            done.append(s)
+            if time.perf_counter() - t0 > budget_s:
+                break
     dt = time.perf_counter() - t0
     nbytes = algorithmic_bytes(context_lens=lens[done].tolist(), num_heads=args["num_heads"],
                                num_kv_heads=args["num_kv_heads"], head_size=args["head_size"],
                                block_size=args["block_size"], alibi=bool(args.get("alibi")))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "host_cpus": os.cpu_count(), "kind": "oracle",
-            "sample": f"{len(done)} of {args['num_seqs']} sequences of the same workload "
-                      f"({dt:.1f} s wall, fp64 numpy)",
+            "sample": f"{len(done)} sequence decodes cycling over {n} of the {args['num_seqs']} "
+                      f"sequences of the same workload ({dt:.1f} s wall, fp64 numpy)",
             "seconds_per_sequence": round(dt / len(done), 4)}
 
 
