@@ -50,10 +50,78 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="also time the calls replayed from a HIP graph (GPU time without the "
                          "host launch path; matters for small, launch-bound batches)")
+    ap.add_argument("--op", default="decode", choices=["decode", "gather", "cache_write"],
+                    help="decode (default), or one of the row-copy kernels at the gather "
+                         "page's shapes (40 heads, D 128, block 8, 1024 blocks, fp16)")
+    ap.add_argument("--tokens", type=int, default=2048, help="rows per call for --op gather/cache_write")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of decoding, run --steps device-to-device copies of MIB MiB "
                          "(reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_bytes_once(num_tokens, num_kv_heads, head_size, elem_bytes):
+    """K and V bytes of num_tokens rows, each counted once."""
+    return 2 * num_tokens * num_kv_heads * head_size * elem_bytes
+
+
+def pages_gib_per_s(num_tokens, num_kv_heads, head_size, elem_bytes, seconds):
+    """The gather page's throughput convention: K+V bytes once, in GiB/s."""
+    return copy_bytes_once(num_tokens, num_kv_heads, head_size, elem_bytes) / seconds / 2 ** 30
+
+
+def bench_copy(op, steps, warmup, num_tokens):
+    """Time gather_cached_kv or paged_kv_cache_write at the gather page's shapes."""
+    import torch
+
+    from decode_attention_paged_06_amd import gather_cached_kv, paged_kv_cache_write
+    from workloads import gather_inputs
+
+    H, D, BS, NB = 40, 128, 8, 1024
+    dev = torch.device("cuda:0")
+    sets = []
+    # rotate pools so the ~2 GiB working set defeats the 256 MB last-level cache
+    for i in range(max(1, -(-ROTATE_BYTES // (2 * NB * H * BS * D * 2)))):
+        g = gather_inputs(num_tokens=num_tokens, num_kv_heads=H, head_size=D, block_size=BS,
+                          num_blocks=NB, dtype="f16", seed=29 + i, device=dev)
+        rows = (torch.empty((num_tokens, H, D), dtype=torch.float16, device=dev),
+                torch.empty((num_tokens, H, D), dtype=torch.float16, device=dev))
+        sets.append((g, rows))
+
+    def step(i):
+        g, (a, b) = sets[i % len(sets)]
+        if op == "gather":
+            gather_cached_kv(a, b, g.key_cache, g.value_cache, g.slot_mapping, BS)
+        else:
+            paged_kv_cache_write(g.key_cache, g.value_cache, a, b, g.slot_mapping, BS)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # replay from a HIP graph: small copies are otherwise bound by the host launch path
+    ncap = max(20, len(sets))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(ncap):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // ncap)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / (reps * ncap)
+    once = copy_bytes_once(num_tokens, H, D, 2)
+    moved = 2 * once + 4 * num_tokens  # read and write every row, plus the slots
+    print(json.dumps({"op": op, "num_tokens": num_tokens, "num_kv_heads": H, "head_size": D,
+                      "block_size": BS, "num_blocks": NB, "dtype": "f16", "us_per_call": round(sec * 1e6, 3),
+                      "GB/s_read_plus_write": round(moved / sec / 1e9, 2),
+                      "pct_of_hbm_peak": round(100 * moved / sec / 1e9 / HBM_PEAK_GBPS, 2),
+                      "pages_convention_GiB/s": round(pages_gib_per_s(num_tokens, H, D, 2, sec), 2),
+                      "input_sets_rotated": len(sets)}), flush=True)
 
 
 def calibrate_copy(mib, steps):
@@ -157,6 +225,9 @@ def main():
         sys.exit(2)
     if a.calibrate_copy:
         calibrate_copy(a.calibrate_copy, a.steps)
+        return
+    if a.op != "decode":
+        bench_copy(a.op, a.steps, a.warmup, a.tokens)
         return
 
     import torch

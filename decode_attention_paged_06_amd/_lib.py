@@ -18,7 +18,7 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_E
 
 # Every symbol include/paged_attention.h declares.
 EXPORTS = ("paged_attention_decode", "paged_attention_workspace_bytes", "paged_attention_plan",
-           "gather_cached_kv", "pa_status_string", "pa_last_error")
+           "gather_cached_kv", "paged_kv_cache_write", "pa_status_string", "pa_last_error")
 
 
 class PaDims(ctypes.Structure):
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.paged_attention_plan.restype = ctypes.c_int
     L.gather_cached_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     L.gather_cached_kv.restype = ctypes.c_int
+    L.paged_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.paged_kv_cache_write.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_last_error.argtypes = []

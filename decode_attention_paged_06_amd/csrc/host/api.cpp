@@ -31,8 +31,11 @@ int ok() {
 
 constexpr size_t kWsAlign = 256;
 constexpr int kMaxDevices = 64;
-// Workgroups per CU the auto plan aims for before it splits contexts.
+// Workgroups per CU the auto plan aims for before it splits contexts; groups
+// of more than 16 heads (several MFMA head tiles sharing every K/V block) are
+// split finer, which measured best for 48-head MQA with ragged lengths.
 constexpr int kTargetGroupsPerCu = 2;
+constexpr int kTargetGroupsPerCuMultiTile = 4;
 // Smallest partition the auto plan makes: two blocks per wave.
 constexpr int kMinPartitionBlocks = 2 * pa::kWaves;
 
@@ -136,7 +139,9 @@ int make_plan(const pa_dims* d, size_t ws_bytes, const pa_opts* o, bool unlimite
             ? (group + pa::valu_heads_per_workgroup(group) - 1) / pa::valu_heads_per_workgroup(group)
             : 1;
     const long long units = (long long)d->num_seqs * d->num_kv_heads * chunks;
-    const long long target = (long long)kTargetGroupsPerCu * cus;
+    const bool multi_tile = engine == PA_ENGINE_MFMA && pa::mfma_head_tiles(group) > 1;
+    const long long target =
+        (long long)(multi_tile ? kTargetGroupsPerCuMultiTile : kTargetGroupsPerCu) * cus;
     if (units > 0 && units < target && maxb > kMinPartitionBlocks) {
       long long want = (target + units - 1) / units;
       PB = (int)((maxb + want - 1) / want);
@@ -266,10 +271,9 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
   return ok();
 }
 
-int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
-                     const void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
-                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                     int32_t num_blocks, int32_t dtype, pa_stream_t stream) {
+// Shared checks of the two row-copy entry points.
+static int check_copy_args(int32_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                    int32_t block_size, int32_t num_blocks, int32_t dtype) {
   if (dtype != PA_F16 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
   if (num_tokens < 0 || num_kv_heads <= 0 || block_size <= 0 || num_blocks <= 0)
     return fail(PA_ERR_INVALID_ARG, "num_tokens %d, num_kv_heads %d, block_size %d, num_blocks %d",
@@ -280,6 +284,34 @@ int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
     return fail(PA_ERR_INVALID_ARG, "num_tokens * num_kv_heads * head_size too large");
   if ((unsigned long long)num_blocks * block_size > 0x7fffffffULL)
     return fail(PA_ERR_INVALID_ARG, "num_blocks * block_size exceeds the int32 slot range");
+  return PA_OK;
+}
+
+int paged_kv_cache_write(void* key_cache, void* value_cache, const void* key, const void* value,
+                         const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                         pa_stream_t stream) {
+  int st = check_copy_args(num_tokens, num_kv_heads, head_size, block_size, num_blocks, dtype);
+  if (st) return st;
+  if (num_tokens == 0) return ok();
+  if (!key_cache || !value_cache || !key || !value || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(key, 16) ||
+      !aligned(value, 16) || !aligned(slot_mapping, 4))
+    return fail(PA_ERR_ALIGNMENT, "16-bit tensors must be 16-byte aligned, slot_mapping 4-byte");
+  const hipError_t e = pa::launch_cache_write(key_cache, value_cache, key, value, slot_mapping,
+                                              num_tokens, num_kv_heads, head_size, block_size,
+                                              reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "cache write launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
+                     const void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                     int32_t num_blocks, int32_t dtype, pa_stream_t stream) {
+  int st = check_copy_args(num_tokens, num_kv_heads, head_size, block_size, num_blocks, dtype);
+  if (st) return st;
   if (num_tokens == 0) return ok();
   if (!key_out || !value_out || !key_cache || !value_cache || !slot_mapping)
     return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");

@@ -4,20 +4,22 @@
 // over the sequence's cached tokens, reached through its block table ("single
 // query cached KV attention", vLLM PR #420; GQA head mapping of vLLM PR #452).
 //
-// Decomposition.  A workgroup (4 waves) owns the query heads that share one
-// kv head (the GQA group, padded to HT tiles of 16 heads), for one sequence
-// and one context partition.  A head tile is the N = 16 side of the MFMA
-// products and each 16-token cache block is one M = 16 tile:
+// Decomposition.  A workgroup owns the query heads that share one kv head (the
+// GQA group, padded to NT tiles of 16 heads), for one sequence and one context
+// partition.  A head tile is the N = 16 side of the MFMA products and each
+// 16-token cache block is one M = 16 tile:
 //
 //   S^T[t, g]   = sum_d K[t, d] q[g, d]    v_mfma_f32_16x16x32_{f16,bf16}, D/32 steps
 //   O^T[d, g]  += sum_t V[t, d] P[g, t]     v_mfma_f32_16x16x16_{f16,bf16}, D/16 tiles
 //
-// Wave w walks the partition's blocks w, w+4, w+8, ... with a two-deep
-// software pipeline (the next block's K/V loads are in flight while the current
-// block is processed); the four waves' softmax states are merged at the end.
-// Every K/V byte is loaded once per workgroup and feeds all HT head tiles;
-// groups of up to 16 heads (HT = 1) keep their q operands in registers,
-// larger groups re-read them from LDS to save registers.
+// The workgroup has NT x TG waves: wave w computes head tile w % NT over the
+// blocks tg, tg + TG, tg + 2 TG, ... of the partition (tg = w / NT), with a
+// two-deep software pipeline (the next block's K/V loads are in flight while
+// the current block is processed).  The NT tile-waves of a token group walk
+// the same blocks side by side, so a block's K/V comes from HBM once and the
+// other tiles' reads hit the CU's caches (those loads therefore carry no
+// streaming hint); each wave keeps the register footprint of a single tile.  The TG token groups' softmax states are merged
+// at the end.
 //
 // Register layouts (lane = 16 j + r, r = lane % 16, j = lane / 16):
 //   K operand, step i : lane holds K[t = r][16-byte chunk 4i + j]; the load for
@@ -93,8 +95,8 @@ struct VRow<4> {
   static __device__ __forceinline__ T zero() { return make_uint2(0, 0); }
 };
 
-template <typename Fmt, int D, int HT>
-__global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(const DecodeArgs a) {
+template <typename Fmt, int D, int NT, int TG>
+__global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int BS = kBlockSize;
   static_assert(BS == 16, "one cache block is one M = 16 MFMA tile");
   constexpr int CH = D / 8;     // 16-byte chunks per row
@@ -104,8 +106,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(const DecodeAr
   using VT = typename VR::T;
   constexpr float kLog2e = 1.4426950408889634f;
 
+  constexpr int NTHREADS = NT * TG * 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int tile = wave % NT;  // head tile of this wave
+  const int tg = wave / NT;    // token group of this wave
   const int r = lane & 15;
   const int j = lane >> 4;
 
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(const DecodeAr
   if (L <= 0) {
     if (single) {
       uint4* o = reinterpret_cast<uint4*>(a.out) + ((size_t)seq * a.num_heads + h0) * CH;
-      for (int i = threadIdx.x; i < G * CH; i += kWaves * 64) o[i] = make_uint4(0, 0, 0, 0);
+      for (int i = threadIdx.x; i < G * CH; i += NTHREADS) o[i] = make_uint4(0, 0, 0, 0);
     }
     return;
   }
@@ -130,36 +135,24 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(const DecodeAr
   const int blk0 = tok0 / BS;
   const int nblk = (tok1 - tok0 + BS - 1) / BS;
 
-  // ---- shared query load: the group's G rows, zero-padded to HT * 16 ------
-  __shared__ uint4 q_lds[HT * 16 * CH];
+  // ---- shared query load: the group's G rows, zero-padded to NT * 16 ------
+  __shared__ uint4 q_lds[NT * 16 * CH];
   {
     const uint4* qg = reinterpret_cast<const uint4*>(a.q) + ((size_t)seq * a.num_heads + h0) * CH;
-    for (int i = threadIdx.x; i < HT * 16 * CH; i += kWaves * 64)
+    for (int i = threadIdx.x; i < NT * 16 * CH; i += NTHREADS)
       q_lds[i] = (i < G * CH) ? qg[i] : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
-  constexpr bool kQInRegs = HT == 1;
-  uint4 qb[kQInRegs ? NK : 1];
-  if constexpr (kQInRegs) {
+  const int g = tile * 16 + r;  // this lane's head within the group
+  uint4 qb[NK];
 #pragma unroll
-    for (int i = 0; i < NK; ++i) qb[i] = q_lds[r * CH + 4 * i + j];
-  }
-  float slope[HT];
-#pragma unroll
-  for (int n = 0; n < HT; ++n) {
-    const int g = n * 16 + r;
-    slope[n] = (a.alibi != nullptr && g < G) ? a.alibi[h0 + g] * kLog2e : 0.f;
-  }
+  for (int i = 0; i < NK; ++i) qb[i] = q_lds[g * CH + 4 * i + j];
+  const float slope = (a.alibi != nullptr && g < G) ? a.alibi[h0 + g] * kLog2e : 0.f;
 
-  float m[HT], lsum[HT];
-  f32x4_t acc[HT][EPL];
+  float m = kNegBig, lsum = 0.f;
+  f32x4_t acc[EPL];
 #pragma unroll
-  for (int n = 0; n < HT; ++n) {
-    m[n] = kNegBig;
-    lsum[n] = 0.f;
-#pragma unroll
-    for (int t = 0; t < EPL; ++t) acc[n][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int t = 0; t < EPL; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq + blk0;
   // Byte addressing: a wave-uniform block base (SGPRs) plus a small unsigned
@@ -182,54 +175,38 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(const DecodeAr
     const rsrc_t rk = make_rsrc(kbase + boff, BS * D * 2);
     const rsrc_t rv = make_rsrc(vbase + boff, BS * D * 2);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) T.k[i] = buffer_load(rk, k_lane + 64u * i, (uint4*)nullptr);
+    for (int i = 0; i < NK; ++i) T.k[i] = buffer_load<NT == 1>(rk, k_lane + 64u * i, (uint4*)nullptr);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) T.v[i] = buffer_load(rv, v_lane + 2u * D * i, (VT*)nullptr);
+    for (int i = 0; i < 4; ++i) T.v[i] = buffer_load<NT == 1>(rv, v_lane + 2u * D * i, (VT*)nullptr);
   };
 
   auto process = [&](Tile& T, int b) {
     const int tb = (blk0 + b) * BS;
     const int valid = tok1 - tb;
-    uint2 pk[HT];
-    float alpha[HT];
-    bool rescale = false;
 
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int n = 0; n < HT; ++n) {
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NK; ++i) s = Mfma<Fmt>::qk(T.k[i], qb[i], s);
+    float x[4];
 #pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        uint4 qv;
-        if constexpr (kQInRegs) qv = qb[i];
-        else qv = q_lds[(n * 16 + r) * CH + 4 * i + j];
-        s = Mfma<Fmt>::qk(T.k[i], qv, s);
-      }
-      float x[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = 4 * j + v;
-        const float z = fmaf(s[v], a.scale_log2, slope[n] * (float)(tb + t - qpos));
-        x[v] = t < valid ? z : kNegBig;
-      }
-      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float mn = fmaxf(m[n], mx);
-      alpha[n] = fast_exp2(m[n] - mn);
-      rescale |= alpha[n] != 1.f;
-      m[n] = mn;
-      const uint32_t p01 = Fmt::pack(fast_exp2(x[0] - mn), fast_exp2(x[1] - mn));
-      const uint32_t p23 = Fmt::pack(fast_exp2(x[2] - mn), fast_exp2(x[3] - mn));
-      pk[n] = make_uint2(p01, p23);
-      lsum[n] = fmaf(lsum[n], alpha[n],
-                     (Fmt::lo(p01) + Fmt::hi(p01)) + (Fmt::lo(p23) + Fmt::hi(p23)));
+    for (int v = 0; v < 4; ++v) {
+      const int t = 4 * j + v;
+      const float z = fmaf(s[v], a.scale_log2, slope * (float)(tb + t - qpos));
+      x[v] = t < valid ? z : kNegBig;
     }
-    if (wave_any(rescale)) {
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    const uint32_t p01 = Fmt::pack(fast_exp2(x[0] - mn), fast_exp2(x[1] - mn));
+    const uint32_t p23 = Fmt::pack(fast_exp2(x[2] - mn), fast_exp2(x[3] - mn));
+    const uint2 pk = make_uint2(p01, p23);
+    lsum = fmaf(lsum, alpha, (Fmt::lo(p01) + Fmt::hi(p01)) + (Fmt::lo(p23) + Fmt::hi(p23)));
+    if (wave_any(alpha != 1.f)) {
 #pragma unroll
-      for (int n = 0; n < HT; ++n) {
-#pragma unroll
-        for (int t = 0; t < EPL; ++t) acc[n][t] *= alpha[n];
-      }
+      for (int t = 0; t < EPL; ++t) acc[t] *= alpha;
     }
 
     if (valid < BS) {  // last block of a sequence: slots past L may hold NaN
@@ -245,118 +222,106 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(const DecodeAr
       const uint32_t a2 = VR::word(T.v[2], w), a3 = VR::word(T.v[3], w);
       const uint2 vt = (t & 1) ? make_uint2(pack_hi_hi(a0, a1), pack_hi_hi(a2, a3))
                                : make_uint2(pack_lo_lo(a0, a1), pack_lo_lo(a2, a3));
-#pragma unroll
-      for (int n = 0; n < HT; ++n) acc[n][t] = Mfma<Fmt>::pv(vt, pk[n], acc[n][t]);
+      acc[t] = Mfma<Fmt>::pv(vt, pk, acc[t]);
     }
   };
 
   // Software pipeline: the loads of the wave's next block are in flight while
   // the current block is processed (two register tiles, used alternately).
   Tile ta, tb2;
-  int b = wave;
+  int b = tg;
   if (b < nblk) load(ta, b);
   while (b < nblk) {
-    const int b1 = b + kWaves;
+    const int b1 = b + TG;
     if (b1 < nblk) load(tb2, b1);
     process(ta, b);
     if (b1 >= nblk) break;
-    const int b2 = b1 + kWaves;
+    const int b2 = b1 + TG;
     if (b2 < nblk) load(ta, b2);
     process(tb2, b1);
     b = b2;
   }
 
   // ---- complete the per-lane sums over the 4 lane groups -------------------
-#pragma unroll
-  for (int n = 0; n < HT; ++n) {
-    lsum[n] += shfl_xor(lsum[n], 16);
-    lsum[n] += shfl_xor(lsum[n], 32);
-  }
+  lsum += shfl_xor(lsum, 16);
+  lsum += shfl_xor(lsum, 32);
 
-  // ---- merge the waves into wave 0 (fixed order: deterministic) ------------
-  __shared__ f32x4_t mrg_acc[HT][EPL][64];
-  __shared__ float mrg_m[HT][64];
-  __shared__ float mrg_l[HT][64];
-  for (int w = 1; w < kWaves; ++w) {
-    __syncthreads();
-    if (wave == w) {
+  // ---- merge the token groups into group 0 (fixed order: deterministic) ----
+  if constexpr (TG > 1) {
+    __shared__ f32x4_t mrg_acc[NT][EPL][64];
+    __shared__ float mrg_m[NT][64];
+    __shared__ float mrg_l[NT][64];
+    for (int k = 1; k < TG; ++k) {
+      __syncthreads();
+      if (tg == k) {
+        mrg_m[tile][lane] = m;
+        mrg_l[tile][lane] = lsum;
 #pragma unroll
-      for (int n = 0; n < HT; ++n) {
-        mrg_m[n][lane] = m[n];
-        mrg_l[n][lane] = lsum[n];
-#pragma unroll
-        for (int t = 0; t < EPL; ++t) mrg_acc[n][t][lane] = acc[n][t];
+        for (int t = 0; t < EPL; ++t) mrg_acc[tile][t][lane] = acc[t];
       }
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int n = 0; n < HT; ++n) {
-        const float mo = mrg_m[n][lane];
-        const float mn = fmaxf(m[n], mo);
-        const float f = fast_exp2(m[n] - mn);
+      __syncthreads();
+      if (tg == 0) {
+        const float mo = mrg_m[tile][lane];
+        const float mn = fmaxf(m, mo);
+        const float f = fast_exp2(m - mn);
         const float fo = fast_exp2(mo - mn);
-        lsum[n] = lsum[n] * f + mrg_l[n][lane] * fo;
+        lsum = lsum * f + mrg_l[tile][lane] * fo;
 #pragma unroll
-        for (int t = 0; t < EPL; ++t) acc[n][t] = acc[n][t] * f + mrg_acc[n][t][lane] * fo;
-        m[n] = mn;
+        for (int t = 0; t < EPL; ++t) acc[t] = acc[t] * f + mrg_acc[tile][t][lane] * fo;
+        m = mn;
       }
     }
   }
 
   // ---- finalise ---------------------------------------------------------------
-  if (wave != 0) return;
+  if (tg != 0 || g >= G) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const size_t row = (size_t)seq * a.num_heads + h0 + g;
+  if (single) {
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + row * D;
 #pragma unroll
-  for (int n = 0; n < HT; ++n) {
-    const int g = n * 16 + r;
-    if (g >= G) continue;
-    const float inv = lsum[n] > 0.f ? 1.f / lsum[n] : 0.f;
-    const size_t row = (size_t)seq * a.num_heads + h0 + g;
-    if (single) {
-      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + row * D;
+    for (int v = 0; v < 4; ++v) {
+      uint32_t wv[EPL / 2];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        uint32_t wv[EPL / 2];
-#pragma unroll
-        for (int t = 0; t < EPL; t += 2)
-          wv[t / 2] = Fmt::pack(acc[n][t][v] * inv, acc[n][t + 1][v] * inv);
-        VT o;
-        if constexpr (EPL == 8) o = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-        else o = make_uint2(wv[0], wv[1]);
-        *reinterpret_cast<VT*>(orow + EPL * (4 * j + v)) = o;
-      }
-    } else {
-      const size_t slot = row * a.num_partitions + part;
-      float* orow = a.ws_o + slot * D;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-#pragma unroll
-        for (int t = 0; t < EPL; t += 4)
-          *reinterpret_cast<float4*>(orow + EPL * (4 * j + v) + t) =
-              make_float4(acc[n][t][v] * inv, acc[n][t + 1][v] * inv, acc[n][t + 2][v] * inv,
-                          acc[n][t + 3][v] * inv);
-      }
-      if (j == 0) reinterpret_cast<float2*>(a.ws_ml)[slot] = make_float2(m[n], lsum[n]);
+      for (int t = 0; t < EPL; t += 2) wv[t / 2] = Fmt::pack(acc[t][v] * inv, acc[t + 1][v] * inv);
+      VT o;
+      if constexpr (EPL == 8) o = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      else o = make_uint2(wv[0], wv[1]);
+      *reinterpret_cast<VT*>(orow + EPL * (4 * j + v)) = o;
     }
+  } else {
+    const size_t slot = row * a.num_partitions + part;
+    float* orow = a.ws_o + slot * D;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+#pragma unroll
+      for (int t = 0; t < EPL; t += 4)
+        *reinterpret_cast<float4*>(orow + EPL * (4 * j + v) + t) =
+            make_float4(acc[t][v] * inv, acc[t + 1][v] * inv, acc[t + 2][v] * inv,
+                        acc[t + 3][v] * inv);
+    }
+    if (j == 0) reinterpret_cast<float2*>(a.ws_ml)[slot] = make_float2(m, lsum);
   }
 }
 
 namespace {
 
-template <typename Fmt, int D, int HT>
+template <typename Fmt, int D, int NT, int TG>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.num_kv_heads, a.num_seqs, a.num_partitions);
-  decode_mfma_kernel<Fmt, D, HT><<<grid, kWaves * 64, 0, s>>>(a);
+  decode_mfma_kernel<Fmt, D, NT, TG><<<grid, NT * TG * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
+// Head tiles NT = ceil(G / 16); token groups TG chosen so a workgroup has
+// 4 waves where possible (3 x 2 = 6 for 48-head groups).
 template <typename Fmt, int D>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  switch ((a.group + 15) / 16) {
-    case 1: return launch_t<Fmt, D, 1>(a, s);
-    case 2: return launch_t<Fmt, D, 2>(a, s);
-    case 3: return launch_t<Fmt, D, 3>(a, s);
-    default: return launch_t<Fmt, D, 4>(a, s);
+  switch (mfma_head_tiles(a.group)) {
+    case 1: return launch_t<Fmt, D, 1, 4>(a, s);
+    case 2: return launch_t<Fmt, D, 2, 2>(a, s);
+    case 3: return launch_t<Fmt, D, 3, 2>(a, s);
+    default: return launch_t<Fmt, D, 4, 1>(a, s);
   }
 }
 

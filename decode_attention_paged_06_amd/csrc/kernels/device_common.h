@@ -124,13 +124,17 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
-constexpr int kCacheStream = 2;  // "nt": streaming access, no reuse expected
+// STREAM selects the non-temporal hint: right when one wave consumes the bytes
+// (they are never read again), wrong when sibling waves re-read the same lines
+// through the caches (the hint makes the caches drop them).
+template <bool STREAM>
 __device__ __forceinline__ uint4 buffer_load(rsrc_t r, uint32_t off, uint4*) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCacheStream);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, STREAM ? 2 : 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+template <bool STREAM>
 __device__ __forceinline__ uint2 buffer_load(rsrc_t r, uint32_t off, uint2*) {
-  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCacheStream);
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, STREAM ? 2 : 0);
   return make_uint2(v.x, v.y);
 }
 

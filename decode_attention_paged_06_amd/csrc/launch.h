@@ -41,6 +41,9 @@ inline int valu_heads_per_workgroup(int group) {
   return group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8;
 }
 
+// 16-head MFMA tiles needed for a group of `group` query heads.
+inline int mfma_head_tiles(int group) { return (group + 15) / 16; }
+
 // dtype: 0 = fp16, 1 = bf16 (pa_dtype).  head_size: 64 or 128.
 hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, hipStream_t s);
@@ -49,5 +52,9 @@ hipError_t launch_partition_reduce(const DecodeArgs& a, int dtype, int head_size
 hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                          const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
                          int32_t head_size, int32_t block_size, hipStream_t s);
+
+hipError_t launch_cache_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                              const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_size, int32_t block_size, hipStream_t s);
 
 }  // namespace pa

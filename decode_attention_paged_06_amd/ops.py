@@ -109,5 +109,21 @@ def gather_cached_kv(key_out: torch.Tensor, value_out: torch.Tensor, key_cache: 
     return key_out, value_out
 
 
+def paged_kv_cache_write(key_cache: torch.Tensor, value_cache: torch.Tensor, key: torch.Tensor,
+                         value: torch.Tensor, slot_mapping: torch.Tensor, block_size: int,
+                         stream=None):
+    """Enqueue the bit-exact store of key/value rows ([T, Hkv, D]) into their cache slots."""
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache"), (key, "key"),
+                 (value, "value")):
+        _require(t, n, key_cache.dtype)
+    _require(slot_mapping, "slot_mapping", torch.int32)
+    NB, Hkv, BS, D = key_cache.shape
+    check(lib().paged_kv_cache_write(
+        key_cache.data_ptr(), value_cache.data_ptr(), key.data_ptr(), value.data_ptr(),
+        slot_mapping.data_ptr(), slot_mapping.shape[0], Hkv, D, int(block_size), NB,
+        _DTYPE[key_cache.dtype], _stream_ptr(stream)))
+    return key_cache, value_cache
+
+
 __all__ = ["paged_attention_decode", "paged_attention_plan", "paged_attention_workspace_bytes",
-           "gather_cached_kv", "make_dims", "make_opts", "_lib"]
+           "gather_cached_kv", "paged_kv_cache_write", "make_dims", "make_opts", "_lib"]

@@ -178,6 +178,25 @@ int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
                      int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                      int32_t num_blocks, int32_t dtype, pa_stream_t stream);
 
+/*
+ * paged_kv_cache_write -- store the K/V rows of new tokens into their cache
+ * slots, bit for bit: the cache operation that runs before decode attention
+ * (vLLM PR #2744 discusses its cost at large block sizes).  Inverse of
+ * gather_cached_kv.
+ *
+ * key_cache, value_cache [num_blocks, num_kv_heads, block_size, head_size] dtype (written)
+ * key, value             [num_tokens, num_kv_heads, head_size]             dtype
+ * slot_mapping           [num_tokens] int32; slot = block * block_size + offset.
+ *                        A negative slot (a padding token) stores nothing.
+ * Device-side preconditions: slots < num_blocks * block_size and no two tokens
+ * share a slot (otherwise which row lands there is unspecified).
+ * head_size must be a multiple of 8; pointers to 16-bit data 16-byte aligned.
+ */
+int paged_kv_cache_write(void* key_cache, void* value_cache, const void* key, const void* value,
+                         const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                         pa_stream_t stream);
+
 /* Static description of a status code. */
 const char* pa_status_string(int status);
 

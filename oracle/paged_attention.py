@@ -31,6 +31,10 @@ What it computes (plain definitions, float64, on the exact values of the
   bit for bit.  slot = physical_block * block_size + offset; a negative slot
   yields a zero row.
 
+* kv_cache_write: the cache operation that stores each new token's K/V rows
+  into its slot before attention runs (the cache op whose cost at block size
+  256 vLLM PR #2744 discusses), bit for bit; a negative slot is skipped.
+
 Readings of points the pages leave open (cache layout [NB, Hkv, BS, D], the
 new token already in the cache at position L - 1, L <= 0 giving zeros) are
 listed with the rest of the design notes; every function below states the one
@@ -250,3 +254,23 @@ def gather_cached_kv(key_cache_raw, value_cache_raw, slot_mapping, block_size: i
         k_out[i] = kc[slot // block_size, :, slot % block_size, :]
         v_out[i] = vc[slot // block_size, :, slot % block_size, :]
     return k_out, v_out
+
+
+def kv_cache_write(key_cache_raw, value_cache_raw, key_raw, value_raw, slot_mapping,
+                   block_size: int):
+    """Caches after storing token i's rows at slot_mapping[i]: (key_cache, value_cache) copies.
+
+    key/value [T, Hkv, D] raw 16-bit words; caches [NB, Hkv, BS, D].  Row i goes
+    to block slot // block_size, offset slot % block_size; a negative slot leaves
+    the caches untouched.  Slots are distinct (two tokens never share a slot).
+    """
+    kc = np.array(key_cache_raw, copy=True)
+    vc = np.array(value_cache_raw, copy=True)
+    k = np.asarray(key_raw)
+    v = np.asarray(value_raw)
+    for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64).tolist()):
+        if slot < 0:
+            continue
+        kc[slot // block_size, :, slot % block_size, :] = k[i]
+        vc[slot // block_size, :, slot % block_size, :] = v[i]
+    return kc, vc

@@ -346,10 +346,36 @@ def pin_storage_formats():
     assert ora.round_to_storage(x, "f16").tolist() == [0x3C00, 0x3C00, 0x3C02, 0x7C00]
 
 
+def pin_cache_write_round_trip():
+    """Written rows land where the layout says, others stay, negative slots skip."""
+    rng = _rng(10)
+    NB, Hkv, BS, D, T = 9, 3, 8, 4, 30
+    kc = rng.integers(0, 1 << 16, size=(NB, Hkv, BS, D), dtype=np.uint16)
+    vc = rng.integers(0, 1 << 16, size=(NB, Hkv, BS, D), dtype=np.uint16)
+    k = rng.integers(0, 1 << 16, size=(T, Hkv, D), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=(T, Hkv, D), dtype=np.uint16)
+    slots = rng.permutation(NB * BS)[:T]
+    slots[[3, 17]] = -1
+    kc2, vc2 = ora.kv_cache_write(kc, vc, k, v, slots, BS)
+    touched = np.zeros((NB, BS), dtype=bool)
+    for i, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        b, o = divmod(int(slot), BS)          # block-major slot numbering
+        assert np.array_equal(kc2[b, :, o, :], k[i]) and np.array_equal(vc2[b, :, o, :], v[i])
+        touched[b, o] = True
+    assert np.array_equal(kc2.transpose(0, 2, 1, 3)[~touched], kc.transpose(0, 2, 1, 3)[~touched])
+    assert np.array_equal(vc2.transpose(0, 2, 1, 3)[~touched], vc.transpose(0, 2, 1, 3)[~touched])
+    # the gather reads back exactly what was written
+    kg, vg = ora.gather_cached_kv(kc2, vc2, slots, BS)
+    ok = slots >= 0
+    assert np.array_equal(kg[ok], k[ok]) and np.array_equal(vg[ok], v[ok])
+
+
 PINS = [
     pin_brute_force, pin_dense_library, pin_gather_by_construction,
     pin_sequence_kv_by_construction, pin_block_permutation, pin_context_one,
     pin_identical_keys_mean, pin_identical_keys_alibi, pin_needle, pin_gqa_equals_repeated_mha,
     pin_split_merge, pin_shift_and_linearity, pin_empty_context, pin_poison_ignored,
-    pin_storage_formats,
+    pin_storage_formats, pin_cache_write_round_trip,
 ]

@@ -38,3 +38,42 @@ def test_gather_bit_exact(case, random_bits):
                                      g.slot_mapping.cpu().numpy(), BS)
     assert np.array_equal(raw_u16(ko), rk)
     assert np.array_equal(raw_u16(vo), rv)
+
+
+WRITE_CASES = [
+    # tokens, kv heads, head size, block size, blocks, dtype, negative slots
+    (256, 8, 128, 16, 4096, "bf16", 0),    # one decode step of a 256-sequence batch
+    (4096, 8, 128, 16, 1024, "bf16", 9),   # a prefill chunk
+    (333, 40, 128, 8, 1024, "f16", 3),
+    (17, 3, 8, 5, 11, "f16", 2),
+]
+
+
+@pytest.mark.parametrize("case", WRITE_CASES,
+                         ids=[f"T{c[0]}-H{c[1]}-D{c[2]}-BS{c[3]}" for c in WRITE_CASES])
+def test_cache_write_bit_exact_and_round_trip(case):
+    from decode_attention_paged_06_amd import paged_kv_cache_write
+    dev = device()
+    T, H, D, BS, NB, dtype, neg = case
+    g = gather_inputs(num_tokens=T, num_kv_heads=H, head_size=D, block_size=BS, num_blocks=NB,
+                      dtype=dtype, seed=7 * T + H, random_bits=True, num_negative=neg, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(T)
+    k = torch.randint(-32768, 32768, (T, H, D), generator=gen, dtype=torch.int32,
+                      device=dev).to(torch.int16).view(g.key_cache.dtype)
+    v = torch.randint(-32768, 32768, (T, H, D), generator=gen, dtype=torch.int32,
+                      device=dev).to(torch.int16).view(g.key_cache.dtype)
+    before_k, before_v = raw_u16(g.key_cache), raw_u16(g.value_cache)
+    paged_kv_cache_write(g.key_cache, g.value_cache, k, v, g.slot_mapping, BS)
+    torch.cuda.synchronize()
+    rk, rv = oracle.kv_cache_write(before_k, before_v, raw_u16(k), raw_u16(v),
+                                   g.slot_mapping.cpu().numpy(), BS)
+    assert np.array_equal(raw_u16(g.key_cache), rk)
+    assert np.array_equal(raw_u16(g.value_cache), rv)
+    # reading the same slots back returns the written rows
+    ko = torch.empty_like(k)
+    vo = torch.empty_like(v)
+    gather_cached_kv(ko, vo, g.key_cache, g.value_cache, g.slot_mapping, BS)
+    torch.cuda.synchronize()
+    ok = (g.slot_mapping >= 0).cpu().numpy()
+    assert np.array_equal(raw_u16(ko)[ok], raw_u16(k)[ok])
+    assert np.array_equal(raw_u16(vo)[ok], raw_u16(v)[ok])

@@ -194,6 +194,25 @@ def test_gather_validation(L):
     assert g(None, None, None, None, None, 0, 8, 128, 16, 10, 0, None) == OK
 
 
+def test_cache_write_validation(L):
+    w = L.paged_kv_cache_write
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 9, None) == UNSUPPORTED
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 100, 16, 10, 0, None) == UNSUPPORTED
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, -2, 8, 128, 16, 10, 0, None) == INVALID
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 0, 0, None) == INVALID
+    assert w(FAKE, None, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 0, None) == INVALID
+    assert w(FAKE, FAKE, FAKE + 8, FAKE, FAKE, 4, 8, 128, 16, 10, 0, None) == ALIGN
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE + 1, 4, 8, 128, 16, 10, 0, None) == ALIGN
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 1 << 20, 1 << 12, 0, None) == INVALID
+    assert w(None, None, None, None, None, 0, 8, 128, 16, 10, 1, None) == OK
+
+
+def test_plan_multi_tile_partitions(L):
+    # 48-head MQA, batch 256, contexts up to 8192: four partitions per sequence
+    st, p = plan(L, dims(S=256, Hq=48, Hkv=1, MAXB=512))
+    assert st == OK and p.engine == 2 and p.num_partitions == 4
+
+
 def test_status_strings(L):
     for code in range(7):
         assert L.pa_status_string(code).decode()

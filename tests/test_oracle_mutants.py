@@ -11,7 +11,7 @@ from oracle_pins import PINS
 
 _orig = {name: getattr(ora, name) for name in
          ("kv_head_of", "sequence_kv", "alibi_bias", "attend", "merge_partitions",
-          "gather_cached_kv", "to_float64")}
+          "gather_cached_kv", "to_float64", "kv_cache_write")}
 
 
 def _kv_head_mod(h, Hq, Hkv):
@@ -86,6 +86,21 @@ def _to_f64_bf16_as_f16(raw, dtype):
     return _orig["to_float64"](raw, "f16")
 
 
+def _write_offset_major(kc, vc, k, v, slots, BS):
+    # treats the slot as offset-major (slot % NB, slot // NB): wrong numbering
+    NB = kc.shape[0]
+    kc2, vc2 = np.array(kc, copy=True), np.array(vc, copy=True)
+    for i, slot in enumerate(np.asarray(slots).tolist()):
+        if slot >= 0:
+            kc2[slot % NB, :, slot // NB, :] = k[i]
+            vc2[slot % NB, :, slot // NB, :] = v[i]
+    return kc2, vc2
+
+
+def _write_kv_swapped(kc, vc, k, v, slots, BS):
+    return _orig["kv_cache_write"](kc, vc, v, k, slots, BS)
+
+
 MUTANTS = {
     "head_mapping_modulo": ("kv_head_of", _kv_head_mod),
     "drop_last_token": ("sequence_kv", _seq_drop_last),
@@ -101,6 +116,8 @@ MUTANTS = {
     "gather_wrong_offset": ("gather_cached_kv", _gather_wrong_offset),
     "gather_negative_slot_not_zeroed": ("gather_cached_kv", _gather_no_zero),
     "bf16_decoded_as_f16": ("to_float64", _to_f64_bf16_as_f16),
+    "cache_write_offset_major": ("kv_cache_write", _write_offset_major),
+    "cache_write_k_v_swapped": ("kv_cache_write", _write_kv_swapped),
 }
 
 
