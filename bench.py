@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="override the workload's cache block size (tokens per block)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -239,6 +241,10 @@ def main():
     name = a.workload or HEADLINE[0]
     batch = a.batch or HEADLINE[1]
     args = workload_args(name, batch)
+    if a.block_size:
+        args["block_size"] = a.block_size
+        args.pop("pool_blocks", None)  # pool sized to fit the new block size
+        args.pop("max_blocks_per_seq", None)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 

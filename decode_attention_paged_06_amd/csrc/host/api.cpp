@@ -36,8 +36,8 @@ constexpr int kMaxDevices = 64;
 // split finer, which measured best for 48-head MQA with ragged lengths.
 constexpr int kTargetGroupsPerCu = 2;
 constexpr int kTargetGroupsPerCuMultiTile = 4;
-// Smallest partition the auto plan makes: two blocks per wave.
-constexpr int kMinPartitionBlocks = 2 * pa::kWaves;
+// Smallest partition the auto plan makes: 128 tokens (two 16-row tiles per wave).
+constexpr int kMinPartitionTokens = 128;
 
 std::atomic<int> g_num_cus[kMaxDevices];
 
@@ -62,9 +62,10 @@ int check_dims(const pa_dims* d) {
     return fail(PA_ERR_UNSUPPORTED, "dtype %d (expected PA_F16 or PA_BF16)", d->dtype);
   if (d->head_size != 64 && d->head_size != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_size %d (built for 64 and 128)", d->head_size);
-  if (d->block_size != pa::kBlockSize)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d (built for %d)", d->block_size,
-                pa::kBlockSize);
+  if (d->block_size < pa::kMinBlockSize || d->block_size > pa::kMaxBlockSize ||
+      (d->block_size & (d->block_size - 1)) != 0)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d (a power of two in [%d, %d])", d->block_size,
+                pa::kMinBlockSize, pa::kMaxBlockSize);
   if (d->num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks = %d", d->num_blocks);
   if (d->max_blocks_per_seq <= 0)
     return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq = %d", d->max_blocks_per_seq);
@@ -142,10 +143,11 @@ int make_plan(const pa_dims* d, size_t ws_bytes, const pa_opts* o, bool unlimite
     const bool multi_tile = engine == PA_ENGINE_MFMA && pa::mfma_head_tiles(group) > 1;
     const long long target =
         (long long)(multi_tile ? kTargetGroupsPerCuMultiTile : kTargetGroupsPerCu) * cus;
-    if (units > 0 && units < target && maxb > kMinPartitionBlocks) {
+    const int min_pb = kMinPartitionTokens / d->block_size > 1 ? kMinPartitionTokens / d->block_size : 1;
+    if (units > 0 && units < target && maxb > min_pb) {
       long long want = (target + units - 1) / units;
       PB = (int)((maxb + want - 1) / want);
-      if (PB < kMinPartitionBlocks) PB = kMinPartitionBlocks;
+      if (PB < min_pb) PB = min_pb;
       P = (maxb + PB - 1) / PB;
       // shrink to what the workspace holds
       while (P > 1 && !unlimited && split_workspace(d, P) > ws_bytes) {
@@ -250,6 +252,8 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
   a.group = dims->num_heads / dims->num_kv_heads;
   a.num_partitions = plan.num_partitions;
   a.partition_blocks = plan.partition_size / dims->block_size;
+  a.block_size = dims->block_size;
+  a.block_shift = __builtin_ctz((unsigned)dims->block_size);
   a.ws_o = nullptr;
   a.ws_ml = nullptr;
   if (plan.num_partitions > 1) {

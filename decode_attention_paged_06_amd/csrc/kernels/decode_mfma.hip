@@ -7,19 +7,19 @@
 // Decomposition.  A workgroup owns the query heads that share one kv head (the
 // GQA group, padded to NT tiles of 16 heads), for one sequence and one context
 // partition.  A head tile is the N = 16 side of the MFMA products and each
-// 16-token cache block is one M = 16 tile:
+// 16-row tile of cached tokens is the M = 16 side:
 //
 //   S^T[t, g]   = sum_d K[t, d] q[g, d]    v_mfma_f32_16x16x32_{f16,bf16}, D/32 steps
 //   O^T[d, g]  += sum_t V[t, d] P[g, t]     v_mfma_f32_16x16x16_{f16,bf16}, D/16 tiles
 //
 // The workgroup has NT x TG waves: wave w computes head tile w % NT over the
-// blocks tg, tg + TG, tg + 2 TG, ... of the partition (tg = w / NT), with a
-// two-deep software pipeline (the next block's K/V loads are in flight while
-// the current block is processed).  The NT tile-waves of a token group walk
+// 16-row tiles tg, tg + TG, tg + 2 TG, ... of the partition (tg = w / NT), with
+// a two-deep software pipeline (the next tile's K/V loads are in flight while
+// the current tile is processed).  The NT tile-waves of a token group walk
 // the same blocks side by side, so a block's K/V comes from HBM once and the
 // other tiles' reads hit the CU's caches (those loads therefore carry no
-// streaming hint); each wave keeps the register footprint of a single tile.  The TG token groups' softmax states are merged
-// at the end.
+// streaming hint); each wave keeps the register footprint of a single tile.
+// The TG token groups' softmax states are merged at the end.
 //
 // Register layouts (lane = 16 j + r, r = lane % 16, j = lane / 16):
 //   K operand, step i : lane holds K[t = r][16-byte chunk 4i + j]; the load for
@@ -97,8 +97,13 @@ struct VRow<4> {
 
 template <typename Fmt, int D, int NT, int TG>
 __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeArgs a) {
-  constexpr int BS = kBlockSize;
-  static_assert(BS == 16, "one cache block is one M = 16 MFMA tile");
+  // Cache blocks of BS tokens are walked as tiles of TT = min(16, BS) rows, one
+  // M = 16 MFMA tile each: a block of 32..256 tokens is BS/16 tiles sharing one
+  // table lookup; an 8-token block is a half tile whose missing rows read back
+  // as zeros from the bounds-checked buffer loads (and are masked).
+  const int BS = a.block_size;
+  const int TT = BS < 16 ? BS : 16;                                  // tokens per tile
+  const int tpb_shift = a.block_shift > 4 ? a.block_shift - 4 : 0;  // log2(tiles per block)
   constexpr int CH = D / 8;     // 16-byte chunks per row
   constexpr int NK = D / 32;    // q.K MFMA steps
   constexpr int EPL = D / 16;   // V elements per lane per row load = number of P.V tiles
@@ -132,8 +137,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   }
   if (tok0 >= L) return;  // partition past this sequence's end: nothing to do
   const int tok1 = min(L, tok0 + a.partition_blocks * BS);
-  const int blk0 = tok0 / BS;
-  const int nblk = (tok1 - tok0 + BS - 1) / BS;
+  const int tile0 = tok0 / TT;                     // first tile of the partition
+  const int ntiles = (tok1 - tok0 + TT - 1) / TT;  // tiles holding its tokens
 
   // ---- shared query load: the group's G rows, zero-padded to NT * 16 ------
   __shared__ uint4 q_lds[NT * 16 * CH];
@@ -154,8 +159,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 #pragma unroll
   for (int t = 0; t < EPL; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq + blk0;
-  // Byte addressing: a wave-uniform block base (SGPRs) plus a small unsigned
+  const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+  // Byte addressing: a wave-uniform tile base (SGPRs) plus a small unsigned
   // per-lane offset, so every K/V load is one buffer load with a VGPR offset.
   const size_t bstride = (size_t)a.num_kv_heads * BS * D * 2;  // bytes per physical block
   const size_t head_off = (size_t)kvh * BS * D * 2;
@@ -163,26 +168,29 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
   const uint32_t k_lane = (uint32_t)(r * D + j * 8) * 2u;          // step-0 K chunk
   const uint32_t v_lane = (uint32_t)((4 * j) * D + r * EPL) * 2u;  // load-0 V slice
+  const uint32_t tile_bytes = (uint32_t)TT * D * 2;
   const int qpos = L - 1;
 
-  // One cache block's K and V in registers.
+  // One 16-row tile's K and V in registers.
   struct Tile {
     uint4 k[NK];
     VT v[4];
   };
-  auto load = [&](Tile& T, int b) {
-    const size_t boff = (size_t)table[b] * bstride;
-    const rsrc_t rk = make_rsrc(kbase + boff, BS * D * 2);
-    const rsrc_t rv = make_rsrc(vbase + boff, BS * D * 2);
+  auto load = [&](Tile& T, int u) {  // u: tile index within the partition
+    const int ua = tile0 + u;
+    const size_t off = (size_t)table[ua >> tpb_shift] * bstride +
+                       (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * 2);
+    const rsrc_t rk = make_rsrc(kbase + off, tile_bytes);
+    const rsrc_t rv = make_rsrc(vbase + off, tile_bytes);
 #pragma unroll
     for (int i = 0; i < NK; ++i) T.k[i] = buffer_load<NT == 1>(rk, k_lane + 64u * i, (uint4*)nullptr);
 #pragma unroll
     for (int i = 0; i < 4; ++i) T.v[i] = buffer_load<NT == 1>(rv, v_lane + 2u * D * i, (VT*)nullptr);
   };
 
-  auto process = [&](Tile& T, int b) {
-    const int tb = (blk0 + b) * BS;
-    const int valid = tok1 - tb;
+  auto process = [&](Tile& T, int u) {
+    const int tb = (tile0 + u) * TT;       // absolute position of the tile's row 0
+    const int valid = min(tok1 - tb, TT);  // rows [0, valid) are context tokens
 
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       for (int t = 0; t < EPL; ++t) acc[t] *= alpha;
     }
 
-    if (valid < BS) {  // last block of a sequence: slots past L may hold NaN
+    if (valid < 16) {  // last tile of a sequence: slots past L may hold NaN
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (4 * j + i >= valid) T.v[i] = VR::zero();
@@ -229,17 +237,17 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   // Software pipeline: the loads of the wave's next block are in flight while
   // the current block is processed (two register tiles, used alternately).
   Tile ta, tb2;
-  int b = tg;
-  if (b < nblk) load(ta, b);
-  while (b < nblk) {
-    const int b1 = b + TG;
-    if (b1 < nblk) load(tb2, b1);
-    process(ta, b);
-    if (b1 >= nblk) break;
-    const int b2 = b1 + TG;
-    if (b2 < nblk) load(ta, b2);
-    process(tb2, b1);
-    b = b2;
+  int u = tg;
+  if (u < ntiles) load(ta, u);
+  while (u < ntiles) {
+    const int u1 = u + TG;
+    if (u1 < ntiles) load(tb2, u1);
+    process(ta, u);
+    if (u1 >= ntiles) break;
+    const int u2 = u1 + TG;
+    if (u2 < ntiles) load(ta, u2);
+    process(tb2, u1);
+    u = u2;
   }
 
   // ---- complete the per-lane sums over the 4 lane groups -------------------

@@ -6,7 +6,7 @@
 //
 // Work decomposition
 //   workgroup = (kv head, query-head chunk of GT heads, sequence, partition),
-//   4 waves.  Wave w takes the partition's cache blocks w, w+4, w+8, ...
+//   4 waves.  Wave w takes the partition's 16-row tiles w, w+4, w+8, ...
 //   The GT query heads that share the kv head are loaded once into LDS by the
 //   whole workgroup and every lane keeps its 16-byte slice in registers (the
 //   shared query load of vLLM PR #420, done per kv head so each K/V row read
@@ -14,9 +14,9 @@
 //
 // Lane layout inside a wave (D = head size)
 //   TPT = D/8 lanes cover one token row (16 bytes each), TPL = 64/TPT token
-//   rows per wave-wide 16-byte load, BS/TPL loads per 16-token block.  One
-//   load of K (or V) is fully coalesced: TPL consecutive rows of the
-//   contiguous [BS, D] block tile.
+//   rows per wave-wide 16-byte load, 16/TPL loads per 16-row tile of a cache
+//   block.  One load of K (or V) is fully coalesced: TPL consecutive rows of
+//   the contiguous [block_size, D] block tile.
 //   q.k: each lane takes 4 packed dot2 products over its 8 elements, then a
 //   DPP row reduction (mirror / half-mirror / quad swaps) gives every lane of
 //   the row the full dot product -- no LDS, no wave-wide barrier.
@@ -31,12 +31,14 @@ namespace pa {
 
 template <typename Fmt, int D, int GT>
 __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeArgs a) {
-  constexpr int BS = kBlockSize;
+  // Cache blocks are walked as tiles of TT = min(16, BS) rows (see decode_mfma.hip).
+  const int BS = a.block_size;
+  const int TT = BS < 16 ? BS : 16;
+  const int tpb_shift = a.block_shift > 4 ? a.block_shift - 4 : 0;
   constexpr int CH = D / 8;        // 16-byte chunks per token row
   constexpr int TPT = CH;          // lanes per token row
   constexpr int TPL = 64 / TPT;    // token rows per wave-wide load
-  constexpr int NLOAD = BS / TPL;  // loads per block for K, and for V
-  static_assert(BS % TPL == 0, "block must hold a whole number of wave loads");
+  constexpr int NLOAD = 16 / TPL;  // loads per 16-row tile for K, and for V
   static_assert(64 % TPT == 0, "rows must tile the wave");
   constexpr float kLog2e = 1.4426950408889634f;
 
@@ -65,8 +67,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
   }
   if (tok0 >= L) return;  // partition past this sequence's end: nothing to do
   const int tok1 = min(L, tok0 + a.partition_blocks * BS);
-  const int blk0 = tok0 / BS;
-  const int nblk = (tok1 - tok0 + BS - 1) / BS;
+  const int tile0 = tok0 / TT;
+  const int ntiles = (tok1 - tok0 + TT - 1) / TT;
 
   // ---- shared query load --------------------------------------------------
   __shared__ uint4 q_lds[GT * CH];
@@ -95,25 +97,31 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
   }
 
   // ---- block walk -----------------------------------------------------------
-  const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq + blk0;
-  const size_t bstride = (size_t)a.num_kv_heads * BS * CH;  // uint4 per physical block
-  const size_t lane_off = (size_t)kvh * BS * CH + rho * CH + c;
-  const uint4* kbase = reinterpret_cast<const uint4*>(a.k_cache) + lane_off;
-  const uint4* vbase = reinterpret_cast<const uint4*>(a.v_cache) + lane_off;
+  const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+  const size_t bstride = (size_t)a.num_kv_heads * BS * D * 2;  // bytes per physical block
+  const size_t head_off = (size_t)kvh * BS * D * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
+  const uint32_t lane_off = (uint32_t)(rho * CH + c) * 16u;
+  const uint32_t tile_bytes = (uint32_t)TT * D * 2;
   const int qpos = L - 1;  // position of the query token
 
-  for (int b = wave; b < nblk; b += kWaves) {
-    const int phys = table[b];
-    const uint4* kp = kbase + (size_t)phys * bstride;
-    const uint4* vp = vbase + (size_t)phys * bstride;
+  for (int u = wave; u < ntiles; u += kWaves) {
+    const int ua = tile0 + u;
+    const size_t off = (size_t)table[ua >> tpb_shift] * bstride +
+                       (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * 2);
+    const rsrc_t rk = make_rsrc(kbase + off, tile_bytes);
+    const rsrc_t rv = make_rsrc(vbase + off, tile_bytes);
     uint4 kr[NLOAD], vr[NLOAD];
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i) kr[i] = load_nt(kp + i * TPL * CH);
+    for (int i = 0; i < NLOAD; ++i)
+      kr[i] = buffer_load<true>(rk, lane_off + 16u * TPL * CH * i, (uint4*)nullptr);
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i) vr[i] = load_nt(vp + i * TPL * CH);
+    for (int i = 0; i < NLOAD; ++i)
+      vr[i] = buffer_load<true>(rv, lane_off + 16u * TPL * CH * i, (uint4*)nullptr);
 
-    const int tb = (blk0 + b) * BS;  // absolute position of the block's row 0
-    const int valid = tok1 - tb;     // rows [0, valid) are context tokens
+    const int tb = ua * TT;                // absolute position of the tile's row 0
+    const int valid = min(tok1 - tb, TT);  // rows [0, valid) are context tokens
 
     float x[GT][NLOAD];
 #pragma unroll

@@ -26,13 +26,13 @@ __global__ __launch_bounds__(64) void partition_reduce_kernel(const DecodeArgs a
   const size_t row = (size_t)seq * a.num_heads + h;
   uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + row * D + lane * PER;
 
-  const int L = min(a.context_lens[seq], a.max_blocks_per_seq * kBlockSize);
+  const int L = min(a.context_lens[seq], a.max_blocks_per_seq * a.block_size);
   if (L <= 0) {
     if constexpr (PER == 2) *reinterpret_cast<uint32_t*>(orow) = 0u;
     else *orow = 0;
     return;
   }
-  const int ptok = a.partition_blocks * kBlockSize;
+  const int ptok = a.partition_blocks * a.block_size;
   const int nact = min(a.num_partitions, (L + ptok - 1) / ptok);
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + row * a.num_partitions;
   const float* o = a.ws_o + row * a.num_partitions * D + lane * PER;

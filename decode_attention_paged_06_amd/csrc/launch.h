@@ -10,7 +10,8 @@
 
 namespace pa {
 
-constexpr int kBlockSize = 16;   // tokens per cache block the decode kernels are built for
+constexpr int kMinBlockSize = 8;    // decode block sizes: powers of two in [8, 256]
+constexpr int kMaxBlockSize = 256;
 constexpr int kWaves = 4;        // waves per decode workgroup
 constexpr int kMaxGroup = 64;    // largest num_heads / num_kv_heads supported
 
@@ -33,6 +34,8 @@ struct DecodeArgs {
   int32_t group;                // num_heads / num_kv_heads
   int32_t num_partitions;       // 1 = single pass straight to `out`
   int32_t partition_blocks;     // cache blocks per partition
+  int32_t block_size;           // tokens per cache block (a power of two, 8..256)
+  int32_t block_shift;          // log2(block_size)
 };
 
 // Query heads per VALU workgroup for a group size (heads that share a kv head

@@ -73,6 +73,21 @@ def test_group_sizes(engine, group):
 
 
 @pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("block_size", [8, 16, 32, 64, 256])
+def test_block_sizes(engine, block_size):
+    dev = device()
+    lens = [1, 7, 8, 9, 31, 33, 255, 257, 600]
+    for dtype, D in (("bf16", 128), ("f16", 64)):
+        inp = to_device(make(num_seqs=len(lens), num_heads=16, num_kv_heads=2, head_size=D,
+                             block_size=block_size, dtype=dtype, seed=block_size + D,
+                             context_lens=lens, alibi=True, poison=True), dev)
+        ref = oracle_ref(inp)
+        for ps in (-1, 0, max(block_size, 128)):
+            compare(run(inp, engine=engine, partition_size=ps), ref, dtype,
+                    what=f"BS={block_size} D={D} {engine} partition={ps}")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("head_size", [64, 128])
 def test_head_sizes_fp16(engine, head_size):
     dev = device()

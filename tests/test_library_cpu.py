@@ -133,7 +133,9 @@ def test_workspace_bytes_matches_plan(L):
     ("num_heads", 0, INVALID),
     ("num_kv_heads", 0, INVALID),
     ("head_size", 96, UNSUPPORTED),
-    ("block_size", 32, UNSUPPORTED),
+    ("block_size", 12, UNSUPPORTED),     # not a power of two
+    ("block_size", 4, UNSUPPORTED),      # below the smallest built tile
+    ("block_size", 512, UNSUPPORTED),
     ("dtype", 7, UNSUPPORTED),
     ("num_blocks", 0, INVALID),
     ("max_blocks_per_seq", 0, INVALID),
@@ -205,6 +207,14 @@ def test_cache_write_validation(L):
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE + 1, 4, 8, 128, 16, 10, 0, None) == ALIGN
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 1 << 20, 1 << 12, 0, None) == INVALID
     assert w(None, None, None, None, None, 0, 8, 128, 16, 10, 1, None) == OK
+
+
+def test_plan_block_sizes(L):
+    for bs, maxb in ((8, 512), (32, 128), (256, 16)):
+        st, p = plan(L, dims(S=1, BS=bs, MAXB=maxb))
+        assert st == OK and p.num_partitions > 1 and p.partition_size % bs == 0
+        assert p.partition_size >= 128
+        assert p.num_partitions * p.partition_size >= maxb * bs
 
 
 def test_plan_multi_tile_partitions(L):
