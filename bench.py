@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--kv-dtype", default=None, choices=["fp8"],
+                    help="store the K/V caches as FP8 E4M3 (scale 1/16) instead of the query type")
     ap.add_argument("--block-size", type=int, default=0,
                     help="override the workload's cache block size (tokens per block)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -241,6 +243,8 @@ def main():
     name = a.workload or HEADLINE[0]
     batch = a.batch or HEADLINE[1]
     args = workload_args(name, batch)
+    if a.kv_dtype:
+        args["kv_dtype"] = a.kv_dtype
     if a.block_size:
         args["block_size"] = a.block_size
         args.pop("pool_blocks", None)  # pool sized to fit the new block size
@@ -252,7 +256,8 @@ def main():
     lens = first.context_lens.cpu().tolist()
     nbytes = algorithmic_bytes(context_lens=lens, num_heads=args["num_heads"],
                                num_kv_heads=args["num_kv_heads"], head_size=args["head_size"],
-                               block_size=args["block_size"], alibi=bool(args.get("alibi")))
+                               block_size=args["block_size"], alibi=bool(args.get("alibi")),
+                               kv_elem_bytes=first.key_cache.element_size())
     flops = algorithmic_flops(context_lens=lens, num_heads=args["num_heads"],
                               head_size=args["head_size"])
     footprint = sum(t.numel() * t.element_size() for t in
@@ -265,7 +270,8 @@ def main():
                                                       context_lens=lens)))
     outs = [torch.empty_like(s.query) for s in sets]
 
-    dims = make_dims(first.query, first.key_cache, first.block_tables)
+    dims = make_dims(first.query, first.key_cache, first.block_tables, first.k_scale,
+                     first.v_scale)
     opts = make_opts(a.partition_size, a.engine)
     plan = paged_attention_plan(dims, 1 << 40, opts)
     workspace = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
@@ -276,7 +282,8 @@ def main():
         paged_attention_decode(outs[i % nsets], s.query, s.key_cache, s.value_cache,
                                s.block_tables, s.context_lens, s.scale, s.block_size,
                                s.alibi_slopes, workspace=workspace,
-                               partition_size=a.partition_size, engine=a.engine)
+                               partition_size=a.partition_size, engine=a.engine,
+                               k_scale=s.k_scale, v_scale=s.v_scale)
 
     for i in range(a.warmup):
         step(i)

@@ -11,7 +11,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpagedattn.so")
 
-PA_F16, PA_BF16 = 0, 1
+PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_KV_NATIVE, PA_KV_FP8_E4M3 = 0, 1
 PA_ENGINE_AUTO, PA_ENGINE_VALU, PA_ENGINE_MFMA = 0, 1, 2
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_ALIGNMENT",
           4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH", 6: "PA_ERR_DEVICE"}
@@ -25,7 +26,9 @@ class PaDims(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
-                ("max_blocks_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("max_blocks_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("kv_format", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
 
 
 class PaOpts(ctypes.Structure):

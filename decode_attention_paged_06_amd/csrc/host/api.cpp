@@ -71,8 +71,17 @@ int check_dims(const pa_dims* d) {
     return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq = %d", d->max_blocks_per_seq);
   if ((long long)d->max_blocks_per_seq * d->block_size > (1LL << 30))
     return fail(PA_ERR_INVALID_ARG, "context bound max_blocks_per_seq * block_size too large");
+  if (d->kv_format != PA_KV_NATIVE && d->kv_format != PA_KV_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "kv_format %d", d->kv_format);
+  if (d->kv_format == PA_KV_FP8_E4M3) {
+    const float inf = __builtin_inff();
+    if (!(d->k_scale > 0.f) || !(d->v_scale > 0.f) || d->k_scale == inf || d->v_scale == inf)
+      return fail(PA_ERR_INVALID_ARG, "fp8 caches need finite positive k_scale and v_scale");
+  }
   return PA_OK;
 }
+
+size_t elem_bytes(int32_t dtype) { return dtype == PA_FP8_E4M3 ? 1 : 2; }
 
 int current_num_cus(int* out) {
   int dev = 0;
@@ -244,7 +253,10 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.alibi = alibi_slopes;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  const bool kv_fp8 = dims->kv_format == PA_KV_FP8_E4M3;
+  // the key scale folds into the logit scale, the value scale into the output
+  a.scale_log2 = scale * 1.4426950408889634f * (kv_fp8 ? dims->k_scale : 1.f);
+  a.v_scale = kv_fp8 ? dims->v_scale : 1.f;
   a.num_seqs = dims->num_seqs;
   a.num_heads = dims->num_heads;
   a.num_kv_heads = dims->num_kv_heads;
@@ -265,8 +277,8 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = plan.engine == PA_ENGINE_MFMA
-                     ? pa::launch_decode_mfma(a, dims->dtype, dims->head_size, s)
-                     : pa::launch_decode_valu(a, dims->dtype, dims->head_size, s);
+                     ? pa::launch_decode_mfma(a, dims->dtype, dims->head_size, kv_fp8, s)
+                     : pa::launch_decode_valu(a, dims->dtype, dims->head_size, kv_fp8, s);
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
   if (plan.num_partitions > 1) {
     e = pa::launch_partition_reduce(a, dims->dtype, dims->head_size, s);
@@ -278,13 +290,15 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
 // Shared checks of the two row-copy entry points.
 static int check_copy_args(int32_t num_tokens, int32_t num_kv_heads, int32_t head_size,
                     int32_t block_size, int32_t num_blocks, int32_t dtype) {
-  if (dtype != PA_F16 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (dtype != PA_F16 && dtype != PA_BF16 && dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
   if (num_tokens < 0 || num_kv_heads <= 0 || block_size <= 0 || num_blocks <= 0)
     return fail(PA_ERR_INVALID_ARG, "num_tokens %d, num_kv_heads %d, block_size %d, num_blocks %d",
                 num_tokens, num_kv_heads, block_size, num_blocks);
-  if (head_size <= 0 || head_size % 8 != 0)
-    return fail(PA_ERR_UNSUPPORTED, "head_size %d (must be a positive multiple of 8)", head_size);
-  if ((unsigned long long)num_tokens * num_kv_heads * (head_size / 8) >= (1ULL << 32))
+  const long long row_bytes = (long long)head_size * elem_bytes(dtype);
+  if (head_size <= 0 || row_bytes % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "head_size %d (a row must be a multiple of 16 bytes)", head_size);
+  if ((unsigned long long)num_tokens * num_kv_heads * (row_bytes / 16) >= (1ULL << 32))
     return fail(PA_ERR_INVALID_ARG, "num_tokens * num_kv_heads * head_size too large");
   if ((unsigned long long)num_blocks * block_size > 0x7fffffffULL)
     return fail(PA_ERR_INVALID_ARG, "num_blocks * block_size exceeds the int32 slot range");
@@ -304,7 +318,8 @@ int paged_kv_cache_write(void* key_cache, void* value_cache, const void* key, co
       !aligned(value, 16) || !aligned(slot_mapping, 4))
     return fail(PA_ERR_ALIGNMENT, "16-bit tensors must be 16-byte aligned, slot_mapping 4-byte");
   const hipError_t e = pa::launch_cache_write(key_cache, value_cache, key, value, slot_mapping,
-                                              num_tokens, num_kv_heads, head_size, block_size,
+                                              num_tokens, num_kv_heads,
+                                              head_size * (int32_t)elem_bytes(dtype), block_size,
                                               reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "cache write launch: %s", hipGetErrorString(e));
   return ok();
@@ -323,7 +338,8 @@ int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
       !aligned(value_cache, 16) || !aligned(slot_mapping, 4))
     return fail(PA_ERR_ALIGNMENT, "16-bit tensors must be 16-byte aligned, slot_mapping 4-byte");
   const hipError_t e = pa::launch_gather(key_out, value_out, key_cache, value_cache, slot_mapping,
-                                         num_tokens, num_kv_heads, head_size, block_size,
+                                         num_tokens, num_kv_heads,
+                                         head_size * (int32_t)elem_bytes(dtype), block_size,
                                          reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "gather launch: %s", hipGetErrorString(e));
   return ok();

@@ -45,6 +45,13 @@
 // skipped when no lane's max moved.  P is rounded to the storage type before
 // the P.V product (the matrix cores take 16-bit operands); the sum l uses the
 // same rounded values so the normalisation matches what was accumulated.
+//
+// FP8 caches: the tile is loaded as stored (1 byte per element, half the
+// bytes) and converted exactly to the 16-bit compute format when processed;
+// the key scale is folded into the logit scale and the value scale into the
+// final normalisation, so the products above are unchanged.
+#include <type_traits>
+
 #include "../launch.h"
 #include "device_common.h"
 
@@ -95,7 +102,7 @@ struct VRow<4> {
   static __device__ __forceinline__ T zero() { return make_uint2(0, 0); }
 };
 
-template <typename Fmt, int D, int NT, int TG>
+template <typename Fmt, int D, int NT, int TG, bool KV8>
 __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeArgs a) {
   // Cache blocks of BS tokens are walked as tiles of TT = min(16, BS) rows, one
   // M = 16 MFMA tile each: a block of 32..256 tokens is BS/16 tiles sharing one
@@ -109,6 +116,10 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   constexpr int EPL = D / 16;   // V elements per lane per row load = number of P.V tiles
   using VR = VRow<EPL>;
   using VT = typename VR::T;
+  using KS = KVStore<Fmt, KV8>;                  // cache storage (16-bit or FP8)
+  constexpr int ES = KS::kBytes;                 // bytes per cached element
+  using KRaw = typename KS::Raw8;                // 8 cached K elements as loaded
+  using VRaw = typename std::conditional<EPL == 8, typename KS::Raw8, typename KS::Raw4>::type;
   constexpr float kLog2e = 1.4426950408889634f;
 
   constexpr int NTHREADS = NT * TG * 64;
@@ -162,39 +173,50 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
   // Byte addressing: a wave-uniform tile base (SGPRs) plus a small unsigned
   // per-lane offset, so every K/V load is one buffer load with a VGPR offset.
-  const size_t bstride = (size_t)a.num_kv_heads * BS * D * 2;  // bytes per physical block
-  const size_t head_off = (size_t)kvh * BS * D * 2;
+  const size_t bstride = (size_t)a.num_kv_heads * BS * D * ES;  // bytes per physical block
+  const size_t head_off = (size_t)kvh * BS * D * ES;
   const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
-  const uint32_t k_lane = (uint32_t)(r * D + j * 8) * 2u;          // step-0 K chunk
-  const uint32_t v_lane = (uint32_t)((4 * j) * D + r * EPL) * 2u;  // load-0 V slice
-  const uint32_t tile_bytes = (uint32_t)TT * D * 2;
+  const uint32_t k_lane = (uint32_t)(r * D + j * 8) * ES;          // step-0 K chunk
+  const uint32_t v_lane = (uint32_t)((4 * j) * D + r * EPL) * ES;  // load-0 V slice
+  const uint32_t tile_bytes = (uint32_t)TT * D * ES;
   const int qpos = L - 1;
 
-  // One 16-row tile's K and V in registers.
+  // One 16-row tile's K and V in registers, as stored in the cache.
   struct Tile {
-    uint4 k[NK];
-    VT v[4];
+    KRaw k[NK];
+    VRaw v[4];
   };
   auto load = [&](Tile& T, int u) {  // u: tile index within the partition
     const int ua = tile0 + u;
     const size_t off = (size_t)table[ua >> tpb_shift] * bstride +
-                       (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * 2);
+                       (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
     const rsrc_t rk = make_rsrc(kbase + off, tile_bytes);
     const rsrc_t rv = make_rsrc(vbase + off, tile_bytes);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) T.k[i] = buffer_load<NT == 1>(rk, k_lane + 64u * i, (uint4*)nullptr);
+    for (int i = 0; i < NK; ++i)
+      T.k[i] = KS::template load8<NT == 1>(rk, k_lane + 32u * ES * i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) T.v[i] = buffer_load<NT == 1>(rv, v_lane + 2u * D * i, (VT*)nullptr);
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (EPL == 8) T.v[i] = KS::template load8<NT == 1>(rv, v_lane + (uint32_t)D * ES * i);
+      else T.v[i] = KS::template load4<NT == 1>(rv, v_lane + (uint32_t)D * ES * i);
+    }
   };
 
   auto process = [&](Tile& T, int u) {
     const int tb = (tile0 + u) * TT;       // absolute position of the tile's row 0
     const int valid = min(tok1 - tb, TT);  // rows [0, valid) are context tokens
+    // the compute format of the tile (a no-op for 16-bit caches)
+    uint4 kk[NK];
+    VT vv[4];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) kk[i] = KS::to16(T.k[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vv[i] = KS::to16(T.v[i]);
 
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NK; ++i) s = Mfma<Fmt>::qk(T.k[i], qb[i], s);
+    for (int i = 0; i < NK; ++i) s = Mfma<Fmt>::qk(kk[i], qb[i], s);
     float x[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -220,14 +242,14 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     if (valid < 16) {  // last tile of a sequence: slots past L may hold NaN
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (4 * j + i >= valid) T.v[i] = VR::zero();
+        if (4 * j + i >= valid) vv[i] = VR::zero();
     }
 
 #pragma unroll
     for (int t = 0; t < EPL; ++t) {
       const int w = t >> 1;
-      const uint32_t a0 = VR::word(T.v[0], w), a1 = VR::word(T.v[1], w);
-      const uint32_t a2 = VR::word(T.v[2], w), a3 = VR::word(T.v[3], w);
+      const uint32_t a0 = VR::word(vv[0], w), a1 = VR::word(vv[1], w);
+      const uint32_t a2 = VR::word(vv[2], w), a3 = VR::word(vv[3], w);
       const uint2 vt = (t & 1) ? make_uint2(pack_hi_hi(a0, a1), pack_hi_hi(a2, a3))
                                : make_uint2(pack_lo_lo(a0, a1), pack_lo_lo(a2, a3));
       acc[t] = Mfma<Fmt>::pv(vt, pk, acc[t]);
@@ -283,7 +305,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 
   // ---- finalise ---------------------------------------------------------------
   if (tg != 0 || g >= G) return;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
   const size_t row = (size_t)seq * a.num_heads + h0 + g;
   if (single) {
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + row * D;
@@ -314,30 +336,37 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 
 namespace {
 
-template <typename Fmt, int D, int NT, int TG>
+template <typename Fmt, int D, int NT, int TG, bool KV8>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.num_kv_heads, a.num_seqs, a.num_partitions);
-  decode_mfma_kernel<Fmt, D, NT, TG><<<grid, NT * TG * 64, 0, s>>>(a);
+  decode_mfma_kernel<Fmt, D, NT, TG, KV8><<<grid, NT * TG * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
 // Head tiles NT = ceil(G / 16); token groups TG chosen so a workgroup has
 // 4 waves where possible (3 x 2 = 6 for 48-head groups).
-template <typename Fmt, int D>
+template <typename Fmt, int D, bool KV8>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   switch (mfma_head_tiles(a.group)) {
-    case 1: return launch_t<Fmt, D, 1, 4>(a, s);
-    case 2: return launch_t<Fmt, D, 2, 2>(a, s);
-    case 3: return launch_t<Fmt, D, 3, 2>(a, s);
-    default: return launch_t<Fmt, D, 4, 1>(a, s);
+    case 1: return launch_t<Fmt, D, 1, 4, KV8>(a, s);
+    case 2: return launch_t<Fmt, D, 2, 2, KV8>(a, s);
+    case 3: return launch_t<Fmt, D, 3, 2, KV8>(a, s);
+    default: return launch_t<Fmt, D, 4, 1, KV8>(a, s);
   }
+}
+
+template <typename Fmt, bool KV8>
+hipError_t launch_d(const DecodeArgs& a, int head_size, hipStream_t s) {
+  return head_size == 64 ? launch_g<Fmt, 64, KV8>(a, s) : launch_g<Fmt, 128, KV8>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, hipStream_t s) {
-  if (dtype == 0) return head_size == 64 ? launch_g<F16, 64>(a, s) : launch_g<F16, 128>(a, s);
-  return head_size == 64 ? launch_g<BF16, 64>(a, s) : launch_g<BF16, 128>(a, s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, bool kv_fp8,
+                              hipStream_t s) {
+  if (dtype == 0)
+    return kv_fp8 ? launch_d<F16, true>(a, head_size, s) : launch_d<F16, false>(a, head_size, s);
+  return kv_fp8 ? launch_d<BF16, true>(a, head_size, s) : launch_d<BF16, false>(a, head_size, s);
 }
 
 }  // namespace pa

@@ -29,7 +29,7 @@
 
 namespace pa {
 
-template <typename Fmt, int D, int GT>
+template <typename Fmt, int D, int GT, bool KV8>
 __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeArgs a) {
   // Cache blocks are walked as tiles of TT = min(16, BS) rows (see decode_mfma.hip).
   const int BS = a.block_size;
@@ -98,27 +98,35 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
 
   // ---- block walk -----------------------------------------------------------
   const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
-  const size_t bstride = (size_t)a.num_kv_heads * BS * D * 2;  // bytes per physical block
-  const size_t head_off = (size_t)kvh * BS * D * 2;
+  using KS = KVStore<Fmt, KV8>;  // cache storage: 16-bit, or FP8 converted at use
+  constexpr int ES = KS::kBytes;
+  const size_t bstride = (size_t)a.num_kv_heads * BS * D * ES;  // bytes per physical block
+  const size_t head_off = (size_t)kvh * BS * D * ES;
   const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
-  const uint32_t lane_off = (uint32_t)(rho * CH + c) * 16u;
-  const uint32_t tile_bytes = (uint32_t)TT * D * 2;
+  const uint32_t lane_off = (uint32_t)(rho * D + c * 8) * ES;
+  const uint32_t tile_bytes = (uint32_t)TT * D * ES;
   const int qpos = L - 1;  // position of the query token
 
   for (int u = wave; u < ntiles; u += kWaves) {
     const int ua = tile0 + u;
     const size_t off = (size_t)table[ua >> tpb_shift] * bstride +
-                       (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * 2);
+                       (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
     const rsrc_t rk = make_rsrc(kbase + off, tile_bytes);
     const rsrc_t rv = make_rsrc(vbase + off, tile_bytes);
+    typename KS::Raw8 kraw[NLOAD], vraw[NLOAD];
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i)
+      kraw[i] = KS::template load8<true>(rk, lane_off + (uint32_t)ES * TPL * D * i);
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i)
+      vraw[i] = KS::template load8<true>(rv, lane_off + (uint32_t)ES * TPL * D * i);
     uint4 kr[NLOAD], vr[NLOAD];
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i)
-      kr[i] = buffer_load<true>(rk, lane_off + 16u * TPL * CH * i, (uint4*)nullptr);
-#pragma unroll
-    for (int i = 0; i < NLOAD; ++i)
-      vr[i] = buffer_load<true>(rv, lane_off + 16u * TPL * CH * i, (uint4*)nullptr);
+    for (int i = 0; i < NLOAD; ++i) {
+      kr[i] = KS::to16(kraw[i]);
+      vr[i] = KS::to16(vraw[i]);
+    }
 
     const int tb = ua * TT;                // absolute position of the tile's row 0
     const int valid = min(tok1 - tb, TT);  // rows [0, valid) are context tokens
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
     if (g >= nh) break;
-    const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
+    const float inv = l[g] > 0.f ? a.v_scale / l[g] : 0.f;
     const size_t row = (size_t)seq * a.num_heads + h0 + g;
     if (single) {
       uint4 o;
@@ -250,29 +258,36 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
 
 namespace {
 
-template <typename Fmt, int D, int GT>
+template <typename Fmt, int D, int GT, bool KV8>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const int nhc = (a.group + GT - 1) / GT;
   dim3 grid(a.num_kv_heads * nhc, a.num_seqs, a.num_partitions);
-  decode_valu_kernel<Fmt, D, GT><<<grid, kWaves * 64, 0, s>>>(a);
+  decode_valu_kernel<Fmt, D, GT, KV8><<<grid, kWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <typename Fmt, int D>
+template <typename Fmt, int D, bool KV8>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   switch (valu_heads_per_workgroup(a.group)) {
-    case 1: return launch_t<Fmt, D, 1>(a, s);
-    case 2: return launch_t<Fmt, D, 2>(a, s);
-    case 4: return launch_t<Fmt, D, 4>(a, s);
-    default: return launch_t<Fmt, D, 8>(a, s);
+    case 1: return launch_t<Fmt, D, 1, KV8>(a, s);
+    case 2: return launch_t<Fmt, D, 2, KV8>(a, s);
+    case 4: return launch_t<Fmt, D, 4, KV8>(a, s);
+    default: return launch_t<Fmt, D, 8, KV8>(a, s);
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, hipStream_t s) {
-  if (dtype == 0) return head_size == 64 ? launch_g<F16, 64>(a, s) : launch_g<F16, 128>(a, s);
-  return head_size == 64 ? launch_g<BF16, 64>(a, s) : launch_g<BF16, 128>(a, s);
+template <typename Fmt, bool KV8>
+hipError_t launch_d(const DecodeArgs& a, int head_size, hipStream_t s) {
+  return head_size == 64 ? launch_g<Fmt, 64, KV8>(a, s) : launch_g<Fmt, 128, KV8>(a, s);
+}
+
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, bool kv_fp8,
+                              hipStream_t s) {
+  if (dtype == 0)
+    return kv_fp8 ? launch_d<F16, true>(a, head_size, s) : launch_d<F16, false>(a, head_size, s);
+  return kv_fp8 ? launch_d<BF16, true>(a, head_size, s) : launch_d<BF16, false>(a, head_size, s);
 }
 
 }  // namespace pa

@@ -138,4 +138,62 @@ __device__ __forceinline__ uint2 buffer_load(rsrc_t r, uint32_t off, uint2*) {
   return make_uint2(v.x, v.y);
 }
 
+__device__ __forceinline__ uint32_t buffer_load_b32(rsrc_t r, uint32_t off, bool stream) {
+  return stream ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 2)
+                : (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+// ---- FP8 E4M3 caches ----------------------------------------------------------
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two FP8 E4M3 codes (bytes 0-1, or 2-3 when HI, of w) as the compute format's
+// packed pair.  Exact: every E4M3 value is representable in fp16 and bf16.
+template <typename Fmt, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to(uint32_t w) {
+  const f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return Fmt::pack(f.x, f.y);
+}
+
+// How a cache stores 8 (or 4) consecutive elements of a row and how they become
+// the 16-bit compute format.  Native caches hold the compute format already.
+template <typename Fmt, bool FP8>
+struct KVStore {
+  static constexpr int kBytes = 2;  // bytes per element
+  using Raw8 = uint4;
+  using Raw4 = uint2;
+  static __device__ __forceinline__ uint4 to16(uint4 r) { return r; }
+  static __device__ __forceinline__ uint2 to16(uint2 r) { return r; }
+  template <bool STREAM>
+  static __device__ __forceinline__ Raw8 load8(rsrc_t rs, uint32_t off) {
+    return buffer_load<STREAM>(rs, off, (uint4*)nullptr);
+  }
+  template <bool STREAM>
+  static __device__ __forceinline__ Raw4 load4(rsrc_t rs, uint32_t off) {
+    return buffer_load<STREAM>(rs, off, (uint2*)nullptr);
+  }
+};
+
+template <typename Fmt>
+struct KVStore<Fmt, true> {
+  static constexpr int kBytes = 1;
+  using Raw8 = uint2;
+  using Raw4 = uint32_t;
+  static __device__ __forceinline__ uint4 to16(uint2 r) {
+    return make_uint4(fp8x2_to<Fmt, false>(r.x), fp8x2_to<Fmt, true>(r.x),
+                      fp8x2_to<Fmt, false>(r.y), fp8x2_to<Fmt, true>(r.y));
+  }
+  static __device__ __forceinline__ uint2 to16(uint32_t r) {
+    return make_uint2(fp8x2_to<Fmt, false>(r), fp8x2_to<Fmt, true>(r));
+  }
+  template <bool STREAM>
+  static __device__ __forceinline__ Raw8 load8(rsrc_t rs, uint32_t off) {
+    return buffer_load<STREAM>(rs, off, (uint2*)nullptr);
+  }
+  template <bool STREAM>
+  static __device__ __forceinline__ Raw4 load4(rsrc_t rs, uint32_t off) {
+    return buffer_load_b32(rs, off, STREAM);
+  }
+};
+
 }  // namespace pa

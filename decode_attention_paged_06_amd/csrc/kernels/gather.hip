@@ -6,7 +6,7 @@
 //                        operation that precedes attention in vLLM PR #2744).
 //
 // One thread moves one 16-byte chunk of K and the same chunk of V.  A
-// (token, head) row is head_size * 2 contiguous bytes at both ends, so
+// (token, head) row is head_size * element-size contiguous bytes at both ends, so
 // consecutive threads read and write consecutive 16-byte chunks; a row is
 // never split across a wave boundary for head sizes that divide 64 chunks.
 // Only integer moves: NaN payloads and signed zeros pass through unchanged.
@@ -67,8 +67,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(uint4* __restrict__ k_
 
 hipError_t launch_cache_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                               const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                              int32_t head_size, int32_t block_size, hipStream_t s) {
-  const uint32_t ch = (uint32_t)head_size / 8;
+                              int32_t row_bytes, int32_t block_size, hipStream_t s) {
+  const uint32_t ch = (uint32_t)row_bytes / 16;
   const uint32_t total = (uint32_t)num_tokens * (uint32_t)num_kv_heads * ch;
   uint32_t blocks = (total + 255) / 256;
   if (blocks > 65536u) blocks = 65536u;
@@ -81,8 +81,8 @@ hipError_t launch_cache_write(void* k_cache, void* v_cache, const void* k_new, c
 
 hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                          const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                         int32_t head_size, int32_t block_size, hipStream_t s) {
-  const uint32_t ch = (uint32_t)head_size / 8;
+                         int32_t row_bytes, int32_t block_size, hipStream_t s) {
+  const uint32_t ch = (uint32_t)row_bytes / 16;
   const uint32_t total = (uint32_t)num_tokens * (uint32_t)num_kv_heads * ch;
   const uint32_t threads = 256;
   uint32_t blocks = (total + threads - 1) / threads;

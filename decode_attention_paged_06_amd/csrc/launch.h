@@ -36,6 +36,7 @@ struct DecodeArgs {
   int32_t partition_blocks;     // cache blocks per partition
   int32_t block_size;           // tokens per cache block (a power of two, 8..256)
   int32_t block_shift;          // log2(block_size)
+  float v_scale;                // multiplies the values (1 for 16-bit caches)
 };
 
 // Query heads per VALU workgroup for a group size (heads that share a kv head
@@ -47,17 +48,22 @@ inline int valu_heads_per_workgroup(int group) {
 // 16-head MFMA tiles needed for a group of `group` query heads.
 inline int mfma_head_tiles(int group) { return (group + 15) / 16; }
 
-// dtype: 0 = fp16, 1 = bf16 (pa_dtype).  head_size: 64 or 128.
-hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, hipStream_t s);
+// dtype: 0 = fp16, 1 = bf16 (pa_dtype).  head_size: 64 or 128.  kv_fp8: the
+// caches hold FP8 E4M3 codes (scale_log2 already carries the key scale).
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, bool kv_fp8,
+                              hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, bool kv_fp8,
+                              hipStream_t s);
 hipError_t launch_partition_reduce(const DecodeArgs& a, int dtype, int head_size, hipStream_t s);
 
+// Row copies move row_bytes-long rows (a multiple of 16) between the cache and
+// contiguous [num_tokens, num_kv_heads] row arrays.
 hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                          const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                         int32_t head_size, int32_t block_size, hipStream_t s);
+                         int32_t row_bytes, int32_t block_size, hipStream_t s);
 
 hipError_t launch_cache_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                               const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                              int32_t head_size, int32_t block_size, hipStream_t s);
+                              int32_t row_bytes, int32_t block_size, hipStream_t s);
 
 }  // namespace pa

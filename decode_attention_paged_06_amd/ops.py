@@ -11,17 +11,20 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (PA_BF16, PA_ENGINE_AUTO, PA_ENGINE_MFMA, PA_ENGINE_VALU, PA_F16, PaDims,
-                   PaOpts, PaPlan, check, lib)
+from ._lib import (PA_BF16, PA_ENGINE_AUTO, PA_ENGINE_MFMA, PA_ENGINE_VALU, PA_F16, PA_FP8_E4M3,
+                   PA_KV_FP8_E4M3, PA_KV_NATIVE, PaDims, PaOpts, PaPlan, check, lib)
 
-_DTYPE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+_DTYPE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_FP8_E4M3}
 _ENGINE = {"auto": PA_ENGINE_AUTO, "valu": PA_ENGINE_VALU, "mfma": PA_ENGINE_MFMA}
 
 
-def make_dims(query: torch.Tensor, key_cache: torch.Tensor, block_tables: torch.Tensor) -> PaDims:
+def make_dims(query: torch.Tensor, key_cache: torch.Tensor, block_tables: torch.Tensor,
+              k_scale: float = 1.0, v_scale: float = 1.0) -> PaDims:
     S, Hq, D = query.shape
     NB, Hkv, BS, D2 = key_cache.shape
-    return PaDims(S, Hq, Hkv, D, BS, NB, block_tables.shape[1], _DTYPE[query.dtype])
+    fp8 = key_cache.dtype == torch.float8_e4m3fn
+    return PaDims(S, Hq, Hkv, D, BS, NB, block_tables.shape[1], _DTYPE[query.dtype],
+                  PA_KV_FP8_E4M3 if fp8 else PA_KV_NATIVE, float(k_scale), float(v_scale))
 
 
 def make_opts(partition_size: int = 0, engine: str = "auto", num_cus: int = 0) -> PaOpts:
@@ -60,22 +63,26 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
                            context_lens: torch.Tensor, scale: float, block_size: int,
                            alibi_slopes: Optional[torch.Tensor] = None, stream=None,
                            workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
-                           engine: str = "auto") -> torch.Tensor:
+                           engine: str = "auto", k_scale: float = 1.0,
+                           v_scale: float = 1.0) -> torch.Tensor:
     """Enqueue paged decode attention; writes and returns ``out`` ([S, Hq, D]).
 
-    ``workspace`` (uint8 device tensor) is allocated with torch when omitted
-    and the plan needs one.
+    Caches hold the query's dtype, or torch.float8_e4m3fn with the real values
+    code * k_scale / code * v_scale.  ``workspace`` (uint8 device tensor) is
+    allocated with torch when omitted and the plan needs one.
     """
-    for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
-                 (value_cache, "value_cache")):
-        _require(t, n, query.dtype)
+    _require(out, "out", query.dtype)
+    _require(query, "query", query.dtype)
+    kv_dtype = torch.float8_e4m3fn if key_cache.dtype == torch.float8_e4m3fn else query.dtype
+    _require(key_cache, "key_cache", kv_dtype)
+    _require(value_cache, "value_cache", kv_dtype)
     _require(block_tables, "block_tables", torch.int32)
     _require(context_lens, "context_lens", torch.int32)
     if alibi_slopes is not None:
         _require(alibi_slopes, "alibi_slopes", torch.float32)
     if query.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {query.dtype}")
-    dims = make_dims(query, key_cache, block_tables)
+    dims = make_dims(query, key_cache, block_tables, k_scale, v_scale)
     opts = make_opts(partition_size, engine)
     if workspace is None:
         nbytes = paged_attention_workspace_bytes(dims, opts)

@@ -50,8 +50,16 @@ extern "C" {
 /* Identical to hipStream_t. */
 typedef struct ihipStream_t* pa_stream_t;
 
-/* Storage type of query, caches and output. */
-typedef enum { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
+/* Storage types.  Query and output are PA_F16 or PA_BF16; caches are the
+ * same type, or PA_FP8_E4M3 (OCP FP8 E4M3FN: bias 7, no infinities, NaN =
+ * 0x7F/0xFF) with one fp32 scale per cache tensor (see pa_dims). */
+typedef enum { PA_F16 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
+
+/* Storage of the K/V caches relative to the query type. */
+typedef enum {
+  PA_KV_NATIVE = 0,  /* caches hold the query type (dtype)                      */
+  PA_KV_FP8_E4M3 = 1 /* caches hold FP8 E4M3 codes; value = code * k/v_scale   */
+} pa_kv_format;
 
 /* Status codes. */
 enum {
@@ -72,8 +80,11 @@ enum {
  *   block_tables [num_seqs, max_blocks_per_seq]                       int32
  *   context_lens [num_seqs]                                           int32
  *   alibi_slopes [num_heads]                                          float32, or NULL
- * Supported: head_size 64 or 128; block_size 16; num_heads % num_kv_heads == 0
- * with num_heads / num_kv_heads <= 64; fp16 or bf16. */
+ * Supported: head_size 64 or 128; block_size a power of two in [8, 256];
+ * num_heads % num_kv_heads == 0 with num_heads / num_kv_heads <= 64; query
+ * fp16 or bf16; caches of the query type or FP8 E4M3 (1 byte per element).
+ * The fp8 cache format is this library's reading of the "fp8 kv cache" the
+ * FlashAttention-decode page (vLLM PR #2744) names without defining. */
 typedef struct {
   int32_t num_seqs;
   int32_t num_heads;
@@ -82,7 +93,11 @@ typedef struct {
   int32_t block_size;
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
-  int32_t dtype; /* pa_dtype */
+  int32_t dtype;     /* pa_dtype of query and out: PA_F16 or PA_BF16           */
+  int32_t kv_format; /* pa_kv_format; 0 (native) for 16-bit caches             */
+  float k_scale;     /* FP8 caches: real key = code * k_scale (finite, > 0)    */
+  float v_scale;     /* FP8 caches: real value = code * v_scale; both ignored
+                        for native caches                                      */
 } pa_dims;
 
 /* Which inner engine computes q.K and p.V. */
@@ -170,8 +185,9 @@ int paged_attention_plan(const pa_dims* dims, size_t workspace_bytes, const pa_o
  * slot_mapping        [num_tokens] int32; slot = block * block_size + offset.
  *                     A negative slot writes a zero row.  Slots must be
  *                     < num_blocks * block_size (device-side precondition).
- * head_size must be a multiple of 8; pointers to 16-bit data 16-byte aligned.
- * Any block_size >= 1 is accepted.
+ * dtype: PA_F16, PA_BF16 or PA_FP8_E4M3 (bytes are moved, never converted).
+ * A row (head_size elements) must be a multiple of 16 bytes; data pointers
+ * 16-byte aligned.  Any block_size >= 1 is accepted.
  */
 int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
                      const void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
@@ -190,7 +206,9 @@ int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
  *                        A negative slot (a padding token) stores nothing.
  * Device-side preconditions: slots < num_blocks * block_size and no two tokens
  * share a slot (otherwise which row lands there is unspecified).
- * head_size must be a multiple of 8; pointers to 16-bit data 16-byte aligned.
+ * dtype: PA_F16, PA_BF16 or PA_FP8_E4M3 (bytes are moved, never converted).
+ * A row (head_size elements) must be a multiple of 16 bytes; data pointers
+ * 16-byte aligned.
  */
 int paged_kv_cache_write(void* key_cache, void* value_cache, const void* key, const void* value,
                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,

@@ -70,6 +70,33 @@ def to_float64(raw, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def fp8_e4m3_value(code: int) -> float:
+    """Value of one FP8 E4M3 code (OCP "E4M3FN": bias 7, no infinities, 0x7F/0xFF NaN).
+
+    The pages name an fp8 KV cache without fixing a format; this is the reading
+    taken (the format gfx950's conversion instructions implement).
+    """
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return math.nan
+    if exp == 0:
+        return sign * man * 2.0 ** -9              # subnormal: man/8 * 2^(1-7)
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+_FP8_TABLE = np.array([fp8_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def fp8_to_float64(raw) -> np.ndarray:
+    """Exact float64 values of FP8 E4M3 storage bytes (uint8)."""
+    raw = np.asarray(raw)
+    if raw.dtype != np.uint8:
+        raise TypeError("expected raw uint8 storage bytes")
+    return _FP8_TABLE[raw]
+
+
 def round_to_storage(x, dtype: str) -> np.ndarray:
     """Round float64 values to the 16-bit format with round-to-nearest-even.
 
@@ -141,19 +168,23 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
 
 def _as_f64(x, dtype):
     x = np.asarray(x)
+    if x.dtype == np.uint8:
+        return fp8_to_float64(x)
     return to_float64(x, dtype) if x.dtype == np.uint16 else x.astype(np.float64)
 
 
 def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scale: float,
                  block_size: int, alibi_slopes=None, dtype: Optional[str] = None,
-                 seqs=None) -> np.ndarray:
+                 seqs=None, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Paged decode attention, float64 result [S, Hq, D] (or [len(seqs), Hq, D]).
 
     query [S, Hq, D]; key_cache/value_cache [NB, Hkv, BS, D]; block_tables
     [S, MAXB] int; context_lens [S] int; alibi_slopes [Hq] float32 or None.
     16-bit inputs are passed as raw uint16 storage bits together with
-    ``dtype``; float inputs are used as given.  ``seqs`` restricts the work to
-    a subset of sequences (rows are returned in that order).
+    ``dtype``; float inputs are used as given.  An FP8 E4M3 cache is passed as
+    raw uint8 bytes: its value is the decoded byte times ``k_scale`` (keys) or
+    ``v_scale`` (values), one fp32 scale per cache tensor.  ``seqs`` restricts
+    the work to a subset of sequences (rows are returned in that order).
 
     L <= 0 yields a zero row (a sequence with no context has nothing to
     attend to).
@@ -173,8 +204,8 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scal
         if L <= 0:
             continue
         q = _as_f64(q_all[s], dtype)
-        K = _as_f64(sequence_kv(key_cache, tables[s], L, block_size), dtype)
-        V = _as_f64(sequence_kv(value_cache, tables[s], L, block_size), dtype)
+        K = _as_f64(sequence_kv(key_cache, tables[s], L, block_size), dtype) * float(np.float32(k_scale))
+        V = _as_f64(sequence_kv(value_cache, tables[s], L, block_size), dtype) * float(np.float32(v_scale))
         for h in range(Hq):
             kvh = kv_head_of(h, Hq, Hkv)
             bias = None if slopes is None else alibi_bias(float(slopes[h]), L)

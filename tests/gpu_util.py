@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from decode_attention_paged_06_amd import paged_attention_decode
-from workloads import decode_inputs, raw_u16
+from workloads import decode_inputs, raw_bits, raw_u16
 
 # Max-abs tolerances against the fp64 oracle: fp16 2e-3, bf16 1e-2.
 TOL = {"f16": 2e-3, "bf16": 1e-2}
@@ -34,7 +34,8 @@ def run(inp, engine="auto", partition_size=0, out=None):
         out = torch.full_like(inp.query, float("nan"))
     paged_attention_decode(out, inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
                            inp.context_lens, inp.scale, inp.block_size, inp.alibi_slopes,
-                           partition_size=partition_size, engine=engine)
+                           partition_size=partition_size, engine=engine,
+                           k_scale=inp.k_scale, v_scale=inp.v_scale)
     torch.cuda.synchronize()
     return out
 
@@ -57,13 +58,13 @@ def oracle_ref(inp, seqs=None):
     if not phys:
         phys = [0]
     idx = torch.tensor(phys, dtype=torch.long, device=inp.key_cache.device)
-    kc = raw_u16(inp.key_cache.index_select(0, idx))
-    vc = raw_u16(inp.value_cache.index_select(0, idx))
+    kc = raw_bits(inp.key_cache.view(torch.uint8 if inp.key_cache.element_size() == 1 else torch.int16).index_select(0, idx).view(inp.key_cache.dtype))
+    vc = raw_bits(inp.value_cache.view(torch.uint8 if inp.value_cache.element_size() == 1 else torch.int16).index_select(0, idx).view(inp.value_cache.dtype))
     q = raw_u16(inp.query.index_select(0, torch.tensor(seqs, device=inp.query.device)))
     lens_s = np.minimum(lens[seqs], maxb * BS)
     slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.cpu().numpy()
     return oracle.paged_decode(q, kc, vc, np.array(rows), lens_s, inp.scale, BS, slopes,
-                               dtype=inp.dtype)
+                               dtype=inp.dtype, k_scale=inp.k_scale, v_scale=inp.v_scale)
 
 
 def compare(got: torch.Tensor, ref: np.ndarray, dtype: str, seqs=None, what=""):

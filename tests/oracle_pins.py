@@ -372,10 +372,43 @@ def pin_cache_write_round_trip():
     assert np.array_equal(kg[ok], k[ok]) and np.array_equal(vg[ok], v[ok])
 
 
+def pin_fp8_format():
+    """E4M3FN decoding: hand-worked codes and torch's float8_e4m3fn conversion."""
+    want = {0x00: 0.0, 0x80: -0.0, 0x38: 1.0, 0xB8: -1.0, 0x7E: 448.0, 0x01: 2.0 ** -9,
+            0x08: 2.0 ** -6, 0x07: 7 * 2.0 ** -9, 0x3C: 1.5, 0x54: 12.0, 0x41: 2.25}
+    for code, val in want.items():
+        got = ora.fp8_e4m3_value(code)
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), (code, got)
+    assert math.isnan(ora.fp8_e4m3_value(0x7F)) and math.isnan(ora.fp8_e4m3_value(0xFF))
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = ora.fp8_to_float64(codes)
+    both_nan = np.isnan(lib) & np.isnan(ours)
+    assert np.array_equal(lib[~both_nan], ours[~both_nan]) and both_nan.sum() == 2
+
+
+def pin_fp8_cache_scales():
+    """An fp8 cache with scales equals the float cache holding decoded * scale."""
+    inp = decode_inputs(num_seqs=3, num_heads=4, num_kv_heads=2, head_size=16, block_size=8,
+                        dtype="bf16", seed=5, context_lens=[3, 9, 17], alibi=True,
+                        poison=True, kv_dtype="fp8", kv_scale=0.125)
+    kraw = inp.key_cache.view(torch.uint8).numpy()
+    vraw = inp.value_cache.view(torch.uint8).numpy()
+    got = ora.paged_decode(raw_u16(inp.query), kraw, vraw, inp.block_tables.numpy(),
+                           inp.context_lens.numpy(), inp.scale, 8, inp.alibi_slopes.numpy(),
+                           dtype="bf16", k_scale=0.125, v_scale=0.25)
+    kf = inp.key_cache.to(torch.float64).numpy() * 0.125    # library decoding of the bytes
+    vf = inp.value_cache.to(torch.float64).numpy() * 0.25
+    q = ora.to_float64(raw_u16(inp.query), "bf16")
+    ref = ora.paged_decode(q, kf, vf, inp.block_tables.numpy(), inp.context_lens.numpy(),
+                           inp.scale, 8, inp.alibi_slopes.numpy())
+    assert np.isfinite(got).all() and np.array_equal(got, ref)
+
+
 PINS = [
     pin_brute_force, pin_dense_library, pin_gather_by_construction,
     pin_sequence_kv_by_construction, pin_block_permutation, pin_context_one,
     pin_identical_keys_mean, pin_identical_keys_alibi, pin_needle, pin_gqa_equals_repeated_mha,
     pin_split_merge, pin_shift_and_linearity, pin_empty_context, pin_poison_ignored,
-    pin_storage_formats, pin_cache_write_round_trip,
+    pin_storage_formats, pin_cache_write_round_trip, pin_fp8_format, pin_fp8_cache_scales,
 ]

@@ -215,3 +215,50 @@ def test_stream_argument_is_used():
                                inp.context_lens, inp.scale, 16, None, stream=s, partition_size=64)
     s.synchronize()
     compare(out, ref, "bf16", what="side stream")
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 caches (one scale per cache tensor)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("dtype,head_size", [("bf16", 128), ("f16", 128), ("f16", 64)])
+def test_fp8_cache(engine, dtype, head_size):
+    dev = device()
+    lens = [1, 5, 16, 17, 100, 257, 700]
+    for G, alibi in ((8, False), (1, True), (48, True)):
+        Hkv = 2 if G < 48 else 1
+        inp = to_device(make(num_seqs=len(lens), num_heads=G * Hkv, num_kv_heads=Hkv,
+                             head_size=head_size, block_size=16, dtype=dtype, seed=G + head_size,
+                             context_lens=lens, alibi=alibi, poison=True, kv_dtype="fp8",
+                             kv_scale=0.0625), dev)
+        ref = oracle_ref(inp)
+        for ps in (-1, 0, 64):
+            compare(run(inp, engine=engine, partition_size=ps), ref, dtype,
+                    what=f"fp8 G={G} D={head_size} {dtype} {engine} partition={ps}")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_fp8_context_one_is_exact(engine):
+    """L = 1: out = decoded V * v_scale, exactly representable in bf16."""
+    dev = device()
+    inp = to_device(make(num_seqs=4, num_heads=8, num_kv_heads=2, head_size=128, block_size=16,
+                         dtype="bf16", seed=8, context_lens=1, poison=True, kv_dtype="fp8",
+                         kv_scale=0.125, max_blocks_per_seq=2), dev)
+    got = run(inp, engine=engine, partition_size=-1).float().cpu().numpy()
+    v = inp.value_cache.float().cpu().numpy() * 0.125
+    tables = inp.block_tables.cpu().numpy()
+    for s in range(4):
+        for h in range(8):
+            assert np.array_equal(got[s, h], v[tables[s, 0], h // 4, 0]), (s, h)
+
+
+def test_fp8_workload_full_size():
+    """The GQA ctx-4096 batch-64 workload with an fp8 cache, sampled against the oracle."""
+    dev = device()
+    args = workload_args("gqa_ctx4096", 64)
+    inp = make(device_=dev, poison=True, kv_dtype="fp8", **args)
+    seqs = sample_seqs(64, 12, seed=3)
+    ref = oracle_ref(inp, seqs)
+    for engine in ("auto", "valu"):
+        compare(run(inp, engine=engine), ref, "bf16", seqs, what=f"fp8 gqa4096 b64 {engine}")

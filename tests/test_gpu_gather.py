@@ -77,3 +77,37 @@ def test_cache_write_bit_exact_and_round_trip(case):
     ok = (g.slot_mapping >= 0).cpu().numpy()
     assert np.array_equal(raw_u16(ko)[ok], raw_u16(k)[ok])
     assert np.array_equal(raw_u16(vo)[ok], raw_u16(v)[ok])
+
+
+def test_fp8_rows_copy_bit_exact():
+    """Gather and cache write move FP8 bytes unchanged (NaN codes included)."""
+    from decode_attention_paged_06_amd import paged_kv_cache_write
+    dev = device()
+    T, H, D, BS, NB = 300, 8, 128, 16, 64
+    gen = torch.Generator(device=dev).manual_seed(5)
+    kc = torch.randint(0, 256, (NB, H, BS, D), generator=gen, dtype=torch.int32,
+                       device=dev).to(torch.uint8).view(torch.float8_e4m3fn)
+    vc = torch.randint(0, 256, (NB, H, BS, D), generator=gen, dtype=torch.int32,
+                       device=dev).to(torch.uint8).view(torch.float8_e4m3fn)
+    slots = torch.randperm(NB * BS, generator=torch.Generator().manual_seed(2))[:T].to(torch.int32)
+    slots[7] = -1
+    slots = slots.to(dev)
+    ko = torch.empty((T, H, D), dtype=torch.float8_e4m3fn, device=dev)
+    vo = torch.empty_like(ko)
+    gather_cached_kv(ko, vo, kc, vc, slots, BS)
+    torch.cuda.synchronize()
+    kb = kc.view(torch.uint8).cpu().numpy()
+    vb = vc.view(torch.uint8).cpu().numpy()
+    rk, rv = oracle.gather_cached_kv(kb, vb, slots.cpu().numpy(), BS)
+    assert np.array_equal(ko.view(torch.uint8).cpu().numpy(), rk)
+    assert np.array_equal(vo.view(torch.uint8).cpu().numpy(), rv)
+    nk = torch.randint(0, 256, (T, H, D), generator=gen, dtype=torch.int32,
+                       device=dev).to(torch.uint8).view(torch.float8_e4m3fn)
+    nv = torch.randint(0, 256, (T, H, D), generator=gen, dtype=torch.int32,
+                       device=dev).to(torch.uint8).view(torch.float8_e4m3fn)
+    paged_kv_cache_write(kc, vc, nk, nv, slots, BS)
+    torch.cuda.synchronize()
+    wk, wv = oracle.kv_cache_write(kb, vb, nk.view(torch.uint8).cpu().numpy(),
+                                   nv.view(torch.uint8).cpu().numpy(), slots.cpu().numpy(), BS)
+    assert np.array_equal(kc.view(torch.uint8).cpu().numpy(), wk)
+    assert np.array_equal(vc.view(torch.uint8).cpu().numpy(), wv)

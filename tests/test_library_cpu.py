@@ -148,6 +148,21 @@ def test_plan_rejects_bad_dims(L, field, value, code):
     assert L.pa_last_error().decode()
 
 
+def test_fp8_cache_validation(L):
+    d = dims()
+    d.kv_format = 1                      # FP8 E4M3 caches need positive finite scales
+    assert plan(L, d)[0] == INVALID
+    d.k_scale, d.v_scale = 0.5, float("inf")
+    assert plan(L, d)[0] == INVALID
+    d.v_scale = 0.25
+    assert plan(L, d)[0] == OK
+    d.kv_format = 3
+    assert plan(L, d)[0] == UNSUPPORTED
+    g = L.gather_cached_kv               # fp8 rows of head size 8 are 8 bytes: not 16-byte rows
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 8, 16, 10, 2, None) == UNSUPPORTED
+    assert g(None, None, None, None, None, 0, 8, 16, 16, 10, 2, None) == OK
+
+
 def test_plan_rejects_group_above_limit(L):
     assert plan(L, dims(Hq=128, Hkv=1))[0] == UNSUPPORTED
 

@@ -11,7 +11,7 @@ from oracle_pins import PINS
 
 _orig = {name: getattr(ora, name) for name in
          ("kv_head_of", "sequence_kv", "alibi_bias", "attend", "merge_partitions",
-          "gather_cached_kv", "to_float64", "kv_cache_write")}
+          "gather_cached_kv", "to_float64", "kv_cache_write", "fp8_to_float64")}
 
 
 def _kv_head_mod(h, Hq, Hkv):
@@ -101,6 +101,15 @@ def _write_kv_swapped(kc, vc, k, v, slots, BS):
     return _orig["kv_cache_write"](kc, vc, v, k, slots, BS)
 
 
+def _fp8_bias8(raw):
+    return _orig["fp8_to_float64"](raw) / 2.0   # exponent bias 8 instead of 7
+
+
+def _fp8_no_subnormals(raw):
+    v = _orig["fp8_to_float64"](raw)
+    return np.where((np.asarray(raw) & 0x78) == 0, 0.0, v)
+
+
 MUTANTS = {
     "head_mapping_modulo": ("kv_head_of", _kv_head_mod),
     "drop_last_token": ("sequence_kv", _seq_drop_last),
@@ -118,6 +127,8 @@ MUTANTS = {
     "bf16_decoded_as_f16": ("to_float64", _to_f64_bf16_as_f16),
     "cache_write_offset_major": ("kv_cache_write", _write_offset_major),
     "cache_write_k_v_swapped": ("kv_cache_write", _write_kv_swapped),
+    "fp8_exponent_bias_8": ("fp8_to_float64", _fp8_bias8),
+    "fp8_subnormals_flushed": ("fp8_to_float64", _fp8_no_subnormals),
 }
 
 

@@ -51,16 +51,17 @@ def workload_args(name: str, batch: int) -> dict:
 
 
 def algorithmic_bytes(*, context_lens, num_heads, num_kv_heads, head_size, block_size,
-                      elem_bytes=2, alibi=False) -> int:
+                      elem_bytes=2, alibi=False, kv_elem_bytes=None) -> int:
     """Bytes a decode call must move at minimum.
 
-    K and V of every valid token once per KV head, q read and out written once,
+    K and V of every valid token once per KV head (kv_elem_bytes each, 1 for an
+    FP8 cache), q read and out written once,
     one table entry per used block, the context length of every sequence, and
     the ALiBi slopes when present.
     """
     lens = [int(x) for x in context_lens]
     S = len(lens)
-    kv = sum(lens) * num_kv_heads * head_size * 2 * elem_bytes
+    kv = sum(lens) * num_kv_heads * head_size * 2 * (kv_elem_bytes or elem_bytes)
     qo = 2 * S * num_heads * head_size * elem_bytes
     tables = 4 * sum((L + block_size - 1) // block_size for L in lens)
     return kv + qo + tables + 4 * S + (4 * num_heads if alibi else 0)

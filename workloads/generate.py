@@ -29,7 +29,7 @@ from typing import Optional, Sequence, Union
 import numpy as np
 import torch
 
-DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
+DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
 LengthSpec = Union[int, tuple, Sequence[int]]
 
@@ -48,6 +48,9 @@ class DecodeInputs:
     seed: int
     num_blocks_used: int
     poison_block: Optional[int] = None
+    kv_dtype: str = ""
+    k_scale: float = 1.0
+    v_scale: float = 1.0
     meta: dict = field(default_factory=dict)
 
     @property
@@ -76,9 +79,12 @@ def _lengths(spec: LengthSpec, num_seqs: int, gen: torch.Generator) -> torch.Ten
     return lens
 
 
-def _randn(shape, dtype: str, gen: torch.Generator, device) -> torch.Tensor:
-    # Draw in bounded chunks along dim 0 so that very large pools do not need a
-    # full-size fp32 temporary.
+def _randn(shape, dtype: str, gen: torch.Generator, device, scale: float = 1.0) -> torch.Tensor:
+    """N(0, 1) draws divided by `scale`, rounded to `dtype` (RNE; fp8 is E4M3FN).
+
+    Draws in bounded chunks along dim 0 so that very large pools do not need a
+    full-size fp32 temporary.
+    """
     out = torch.empty(shape, dtype=DTYPES[dtype], device=device)
     if len(shape) == 0 or shape[0] == 0:
         return out
@@ -86,8 +92,11 @@ def _randn(shape, dtype: str, gen: torch.Generator, device) -> torch.Tensor:
     step = max(1, (1 << 27) // max(row, 1))
     for i in range(0, shape[0], step):
         j = min(shape[0], i + step)
-        out[i:j] = torch.randn((j - i,) + tuple(shape[1:]), generator=gen,
-                               dtype=torch.float32, device=device).to(DTYPES[dtype])
+        x = torch.randn((j - i,) + tuple(shape[1:]), generator=gen, dtype=torch.float32,
+                        device=device)
+        if scale != 1.0:
+            x = x / scale
+        out[i:j] = x.to(DTYPES[dtype])
     return out
 
 
@@ -95,12 +104,17 @@ def decode_inputs(*, num_seqs: int, num_heads: int, num_kv_heads: int, head_size
                   block_size: int, dtype: str, seed: int, context_lens: LengthSpec,
                   pool_blocks: Optional[int] = None, max_blocks_per_seq: Optional[int] = None,
                   alibi: bool = False, scale: Optional[float] = None, poison: bool = False,
-                  device: Union[str, torch.device] = "cpu") -> DecodeInputs:
+                  device: Union[str, torch.device] = "cpu", kv_dtype: Optional[str] = None,
+                  kv_scale: float = 0.0625) -> DecodeInputs:
     """Build one seeded decode batch.
 
     pool_blocks=None sizes the pool to fit exactly the blocks the sequences
     use (plus one all-NaN block when ``poison``).  Every used block is
     distinct; the assignment is a random permutation of the pool.
+
+    kv_dtype="fp8" stores K and V as FP8 E4M3 with one scale per cache:
+    the real value is code * kv_scale (draws are divided by kv_scale before
+    rounding, so the real values stay ~N(0, 1)).
 
     poison=True writes NaN into every cache slot no valid token occupies
     (tail slots of each last block and all unused pool blocks) and points
@@ -129,9 +143,11 @@ def decode_inputs(*, num_seqs: int, num_heads: int, num_kv_heads: int, head_size
         pos += nb
 
     dev = torch.Generator(device=device).manual_seed(seed + 1)
+    kv_dtype = kv_dtype or dtype
+    kv_s = kv_scale if kv_dtype == "fp8" else 1.0
     q = _randn((num_seqs, num_heads, head_size), dtype, dev, device)
-    kc = _randn((NB, num_kv_heads, block_size, head_size), dtype, dev, device)
-    vc = _randn((NB, num_kv_heads, block_size, head_size), dtype, dev, device)
+    kc = _randn((NB, num_kv_heads, block_size, head_size), kv_dtype, dev, device, kv_s)
+    vc = _randn((NB, num_kv_heads, block_size, head_size), kv_dtype, dev, device, kv_s)
 
     if poison:
         nan = float("nan")
@@ -156,7 +172,8 @@ def decode_inputs(*, num_seqs: int, num_heads: int, num_kv_heads: int, head_size
                         block_tables=tables.to(device), context_lens=lens.to(device),
                         alibi_slopes=slopes, scale=float(scale), block_size=block_size,
                         dtype=dtype, seed=seed, num_blocks_used=used,
-                        poison_block=poison_block)
+                        poison_block=poison_block, kv_dtype=kv_dtype, k_scale=kv_s,
+                        v_scale=kv_s)
 
 
 @dataclass
@@ -204,3 +221,10 @@ def raw_u16(t: torch.Tensor) -> np.ndarray:
     """The storage bits of a 16-bit float tensor as a host uint16 array."""
     assert t.element_size() == 2
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def raw_bits(t: torch.Tensor) -> np.ndarray:
+    """Storage bits of a 16-bit (uint16) or 8-bit (uint8) float tensor on the host."""
+    if t.element_size() == 1:
+        return t.detach().contiguous().cpu().view(torch.uint8).numpy()
+    return raw_u16(t)
