@@ -54,7 +54,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="also time the calls replayed from a HIP graph (GPU time without the "
                          "host launch path; matters for small, launch-bound batches)")
-    ap.add_argument("--op", default="decode", choices=["decode", "gather", "cache_write"],
+    ap.add_argument("--context", type=int, default=4096, help="context per sequence for --op prefill")
+    ap.add_argument("--new-tokens", type=int, default=512, help="new tokens per sequence for --op prefill")
+    ap.add_argument("--op", default="decode", choices=["decode", "gather", "cache_write", "prefill"],
                     help="decode (default), or one of the row-copy kernels at the gather "
                          "page's shapes (40 heads, D 128, block 8, 1024 blocks, fp16)")
     ap.add_argument("--tokens", type=int, default=2048, help="rows per call for --op gather/cache_write")
@@ -126,6 +128,49 @@ def bench_copy(op, steps, warmup, num_tokens):
                       "pct_of_hbm_peak": round(100 * moved / sec / 1e9 / HBM_PEAK_GBPS, 2),
                       "pages_convention_GiB/s": round(pages_gib_per_s(num_tokens, H, D, 2, sec), 2),
                       "input_sets_rotated": len(sets)}), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
+
+
+def bench_prefill(steps, warmup, batch, context, new_tokens, partition_size):
+    """Time causal multi-query attention: `new_tokens` queries per sequence over a
+    `context`-token paged cache (GQA 64/8, D 128, bf16, block 16)."""
+    import torch
+
+    from decode_attention_paged_06_amd import paged_attention_prefill
+    from workloads import prefill_inputs
+
+    dev = torch.device("cuda:0")
+    inp, q, qs, max_q = prefill_inputs(new_tokens=[new_tokens] * batch, seed=77, device=dev,
+                                       num_seqs=batch, num_heads=64, num_kv_heads=8,
+                                       head_size=128, block_size=16, dtype="bf16",
+                                       context_lens=context)
+    out = torch.empty_like(q)
+
+    def step():
+        paged_attention_prefill(out, q, inp.key_cache, inp.value_cache, inp.block_tables,
+                                inp.context_lens, qs, max_q, inp.scale, 16,
+                                partition_size=partition_size)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / steps
+    # q.K and P.V multiply-adds over the visible (causal) keys of every query
+    keys = sum(context - new_tokens + i + 1 for i in range(new_tokens)) * batch
+    flops = 4 * 64 * 128 * keys
+    print(json.dumps({"op": "prefill", "batch": batch, "context": context,
+                      "new_tokens": new_tokens, "us_per_call": round(sec * 1e6, 2),
+                      "TFLOP/s": round(flops / sec / 1e12, 2),
+                      "pct_of_mfma_peak": round(100 * flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2)}),
+          flush=True)
 
 
 def calibrate_copy(mib, steps):
@@ -229,6 +274,9 @@ def main():
         sys.exit(2)
     if a.calibrate_copy:
         calibrate_copy(a.calibrate_copy, a.steps)
+        return
+    if a.op == "prefill":
+        bench_prefill(a.steps, a.warmup, a.batch or 4, a.context, a.new_tokens, a.partition_size)
         return
     if a.op != "decode":
         bench_copy(a.op, a.steps, a.warmup, a.tokens)

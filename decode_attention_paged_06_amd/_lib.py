@@ -19,7 +19,9 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_E
 
 # Every symbol include/paged_attention.h declares.
 EXPORTS = ("paged_attention_decode", "paged_attention_workspace_bytes", "paged_attention_plan",
-           "gather_cached_kv", "paged_kv_cache_write", "pa_status_string", "pa_last_error")
+           "paged_attention_prefill", "paged_attention_prefill_workspace_bytes",
+           "paged_attention_prefill_plan", "gather_cached_kv", "paged_kv_cache_write",
+           "pa_status_string", "pa_last_error")
 
 
 class PaDims(ctypes.Structure):
@@ -68,6 +70,16 @@ def lib() -> ctypes.CDLL:
     L.paged_attention_plan.argtypes = [ctypes.POINTER(PaDims), sz, ctypes.POINTER(PaOpts),
                                        ctypes.POINTER(PaPlan)]
     L.paged_attention_plan.restype = ctypes.c_int
+    L.paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float,
+                                          i32, vp, vp, ctypes.POINTER(PaDims), vp, sz,
+                                          ctypes.POINTER(PaOpts)]
+    L.paged_attention_prefill.restype = ctypes.c_int
+    L.paged_attention_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PaDims), i32, i32,
+                                                          ctypes.POINTER(PaOpts)]
+    L.paged_attention_prefill_workspace_bytes.restype = sz
+    L.paged_attention_prefill_plan.argtypes = [ctypes.POINTER(PaDims), i32, i32, sz,
+                                               ctypes.POINTER(PaOpts), ctypes.POINTER(PaPlan)]
+    L.paged_attention_prefill_plan.restype = ctypes.c_int
     L.gather_cached_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     L.gather_cached_kv.restype = ctypes.c_int
     L.paged_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]

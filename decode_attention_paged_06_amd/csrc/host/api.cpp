@@ -97,17 +97,37 @@ int current_num_cus(int* out) {
   return PA_OK;
 }
 
+// What one call computes beyond its pa_dims: decode (one new token per
+// sequence) or multi-query (packed new tokens, up to max_new per sequence).
+struct CallShape {
+  bool multi = false;
+  int32_t rows = 0;     // rows of query / out: num_seqs for decode
+  int32_t max_new = 1;  // bound on new tokens per sequence
+};
+
+CallShape decode_shape(const pa_dims* d) {
+  CallShape c;
+  c.rows = d->num_seqs;
+  return c;
+}
+
 // Workspace bytes for P partitions: fp32 partial outputs, then (m, l) pairs.
-size_t split_workspace(const pa_dims* d, int P) {
+size_t split_workspace(const pa_dims* d, const CallShape& c, int P) {
   if (P <= 1) return 0;
-  const size_t rows = (size_t)d->num_seqs * d->num_heads * P;
+  const size_t rows = (size_t)c.rows * d->num_heads * P;
   return align_up(rows * d->head_size * sizeof(float), kWsAlign) + rows * 2 * sizeof(float);
 }
 
-int resolve_engine(const pa_dims* d, const pa_opts* o, int* engine) {
+int resolve_engine(const pa_dims* d, const CallShape& c, const pa_opts* o, int* engine) {
   int e = o ? o->engine : PA_ENGINE_AUTO;
   if (e != PA_ENGINE_AUTO && e != PA_ENGINE_VALU && e != PA_ENGINE_MFMA)
     return fail(PA_ERR_INVALID_ARG, "engine %d", e);
+  if (c.multi) {  // many query rows per key: always the matrix cores
+    if (e == PA_ENGINE_VALU)
+      return fail(PA_ERR_UNSUPPORTED, "multi-query attention runs on the MFMA engine only");
+    *engine = PA_ENGINE_MFMA;
+    return PA_OK;
+  }
   if (e == PA_ENGINE_AUTO) {
     const int group = d->num_heads / d->num_kv_heads;
     e = group >= 4 ? PA_ENGINE_MFMA : PA_ENGINE_VALU;
@@ -116,12 +136,24 @@ int resolve_engine(const pa_dims* d, const pa_opts* o, int* engine) {
   return PA_OK;
 }
 
+// Workgroups per (sequence, kv head): query-head chunks on the VALU path, one
+// on the MFMA decode path, query-row chunks of 64 rows for multi-query calls.
+long long row_chunks(const pa_dims* d, const CallShape& c, int engine) {
+  const int group = d->num_heads / d->num_kv_heads;
+  if (c.multi)
+    return ((long long)c.max_new * group + 16 * pa::kPrefillRowTiles - 1) / (16 * pa::kPrefillRowTiles);
+  if (engine == PA_ENGINE_VALU)
+    return (group + pa::valu_heads_per_workgroup(group) - 1) / pa::valu_heads_per_workgroup(group);
+  return 1;
+}
+
 // The planner.  `unlimited` ignores ws_bytes (used for sizing).
-int make_plan(const pa_dims* d, size_t ws_bytes, const pa_opts* o, bool unlimited, pa_plan* p) {
+int make_plan(const pa_dims* d, const CallShape& c, size_t ws_bytes, const pa_opts* o,
+              bool unlimited, pa_plan* p) {
   int st = check_dims(d);
   if (st) return st;
   int engine = 0;
-  if ((st = resolve_engine(d, o, &engine))) return st;
+  if ((st = resolve_engine(d, c, o, &engine))) return st;
   const int maxb = d->max_blocks_per_seq;
   const int forced = o ? o->partition_size : 0;
   int P = 1, PB = maxb;
@@ -135,21 +167,17 @@ int make_plan(const pa_dims* d, size_t ws_bytes, const pa_opts* o, bool unlimite
     PB = forced / d->block_size;
     P = (maxb + PB - 1) / PB;
     if (P > 65535) return fail(PA_ERR_INVALID_ARG, "partition_size %d gives %d partitions", forced, P);
-    if (P > 1 && !unlimited && split_workspace(d, P) > ws_bytes)
+    if (P > 1 && !unlimited && split_workspace(d, c, P) > ws_bytes)
       return fail(PA_ERR_WORKSPACE, "forced partition_size %d needs %zu workspace bytes, got %zu",
-                  forced, split_workspace(d, P), ws_bytes);
+                  forced, split_workspace(d, c, P), ws_bytes);
   } else if (forced == 0) {
     int cus = o ? o->num_cus : 0;
     if (cus < 0) return fail(PA_ERR_INVALID_ARG, "num_cus = %d", cus);
     if (cus == 0 && (st = current_num_cus(&cus))) return st;
     const int group = d->num_heads / d->num_kv_heads;
-    // workgroups per (sequence, kv head): query-head chunks on the VALU path, one on MFMA
-    const long long chunks =
-        engine == PA_ENGINE_VALU
-            ? (group + pa::valu_heads_per_workgroup(group) - 1) / pa::valu_heads_per_workgroup(group)
-            : 1;
-    const long long units = (long long)d->num_seqs * d->num_kv_heads * chunks;
-    const bool multi_tile = engine == PA_ENGINE_MFMA && pa::mfma_head_tiles(group) > 1;
+    const long long units = (long long)d->num_seqs * d->num_kv_heads * row_chunks(d, c, engine);
+    const bool multi_tile =
+        engine == PA_ENGINE_MFMA && !c.multi && pa::mfma_head_tiles(group) > 1;
     const long long target =
         (long long)(multi_tile ? kTargetGroupsPerCuMultiTile : kTargetGroupsPerCu) * cus;
     const int min_pb = kMinPartitionTokens / d->block_size > 1 ? kMinPartitionTokens / d->block_size : 1;
@@ -159,7 +187,7 @@ int make_plan(const pa_dims* d, size_t ws_bytes, const pa_opts* o, bool unlimite
       if (PB < min_pb) PB = min_pb;
       P = (maxb + PB - 1) / PB;
       // shrink to what the workspace holds
-      while (P > 1 && !unlimited && split_workspace(d, P) > ws_bytes) {
+      while (P > 1 && !unlimited && split_workspace(d, c, P) > ws_bytes) {
         PB *= 2;
         P = (maxb + PB - 1) / PB;
       }
@@ -176,50 +204,16 @@ int make_plan(const pa_dims* d, size_t ws_bytes, const pa_opts* o, bool unlimite
   p->partition_size = PB * d->block_size;
   p->engine = engine;
   p->reserved = 0;
-  p->workspace_bytes = split_workspace(d, P);
+  p->workspace_bytes = split_workspace(d, c, P);
   return PA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* pa_status_string(int status) {
-  switch (status) {
-    case PA_OK: return "ok";
-    case PA_ERR_INVALID_ARG: return "invalid argument";
-    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
-    case PA_ERR_ALIGNMENT: return "misaligned pointer";
-    case PA_ERR_WORKSPACE: return "workspace too small";
-    case PA_ERR_LAUNCH: return "kernel launch failed";
-    case PA_ERR_DEVICE: return "device query failed";
-    default: return "unknown status";
-  }
-}
-
-const char* pa_last_error(void) { return g_last_error; }
-
-int paged_attention_plan(const pa_dims* dims, size_t workspace_bytes, const pa_opts* opts,
-                         pa_plan* plan) {
-  if (plan == nullptr) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
-  pa_plan p;
-  const int st = make_plan(dims, workspace_bytes, opts, false, &p);
-  if (st) return st;
-  *plan = p;
-  return ok();
-}
-
-size_t paged_attention_workspace_bytes(const pa_dims* dims, const pa_opts* opts) {
-  pa_plan p;
-  if (make_plan(dims, 0, opts, true, &p)) return 0;
-  return p.workspace_bytes;
-}
-
-int paged_attention_decode(void* out, const void* query, const void* key_cache,
-                           const void* value_cache, const int32_t* block_tables,
-                           const int32_t* context_lens, float scale, int32_t block_size,
-                           const float* alibi_slopes, pa_stream_t stream, const pa_dims* dims,
-                           void* workspace, size_t workspace_bytes, const pa_opts* opts) {
+// Validation, planning and launch shared by the decode and multi-query calls.
+int run_attention(void* out, const void* query, const void* key_cache, const void* value_cache,
+                  const int32_t* block_tables, const int32_t* context_lens,
+                  const int32_t* query_start, const CallShape& c, float scale, int32_t block_size,
+                  const float* alibi_slopes, pa_stream_t stream, const pa_dims* dims,
+                  void* workspace, size_t workspace_bytes, const pa_opts* opts) {
   int st = check_dims(dims);
   if (st) return st;
   if (block_size != dims->block_size)
@@ -227,18 +221,26 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
                 block_size, dims->block_size);
   if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
     return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-  if (dims->num_seqs == 0) return ok();
-  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+  if (c.multi) {
+    if (c.rows < 0 || c.max_new < 0)
+      return fail(PA_ERR_INVALID_ARG, "num_query_tokens %d, max_query_len %d", c.rows, c.max_new);
+    if (c.max_new > 65535)
+      return fail(PA_ERR_INVALID_ARG, "max_query_len %d exceeds 65535", c.max_new);
+  }
+  if (dims->num_seqs == 0 || c.rows == 0 || c.max_new == 0) return ok();
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      (c.multi && !query_start))
     return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
       !aligned(value_cache, 16))
     return fail(PA_ERR_ALIGNMENT, "out, query and caches must be 16-byte aligned");
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-      (alibi_slopes && !aligned(alibi_slopes, 4)))
-    return fail(PA_ERR_ALIGNMENT, "block_tables, context_lens and alibi_slopes must be 4-byte aligned");
+      (alibi_slopes && !aligned(alibi_slopes, 4)) || (query_start && !aligned(query_start, 4)))
+    return fail(PA_ERR_ALIGNMENT,
+                "block_tables, context_lens, query_start_loc and alibi_slopes must be 4-byte aligned");
 
   pa_plan plan;
-  if ((st = make_plan(dims, workspace ? workspace_bytes : 0, opts, false, &plan))) return st;
+  if ((st = make_plan(dims, c, workspace ? workspace_bytes : 0, opts, false, &plan))) return st;
   if (plan.num_partitions > 1) {
     if (!workspace) return fail(PA_ERR_WORKSPACE, "split plan needs a workspace");
     if (!aligned(workspace, kWsAlign))
@@ -266,25 +268,121 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
   a.partition_blocks = plan.partition_size / dims->block_size;
   a.block_size = dims->block_size;
   a.block_shift = __builtin_ctz((unsigned)dims->block_size);
+  a.query_start = c.multi ? query_start : nullptr;
+  a.max_new_tokens = c.max_new;
+  a.row_chunks = (int32_t)(plan.engine == PA_ENGINE_MFMA ? row_chunks(dims, c, plan.engine) : 1);
   a.ws_o = nullptr;
   a.ws_ml = nullptr;
   if (plan.num_partitions > 1) {
-    const size_t rows = (size_t)dims->num_seqs * dims->num_heads * plan.num_partitions;
+    const size_t rows = (size_t)c.rows * dims->num_heads * plan.num_partitions;
     a.ws_o = static_cast<float*>(workspace);
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        align_up(rows * dims->head_size * sizeof(float), kWsAlign));
   }
+  if ((long long)dims->num_kv_heads * a.row_chunks > 0x7fffffffLL)
+    return fail(PA_ERR_INVALID_ARG, "too many query rows per sequence");
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = plan.engine == PA_ENGINE_MFMA
                      ? pa::launch_decode_mfma(a, dims->dtype, dims->head_size, kv_fp8, s)
                      : pa::launch_decode_valu(a, dims->dtype, dims->head_size, kv_fp8, s);
-  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "attention launch: %s", hipGetErrorString(e));
   if (plan.num_partitions > 1) {
     e = pa::launch_partition_reduce(a, dims->dtype, dims->head_size, s);
     if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reduce launch: %s", hipGetErrorString(e));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_ALIGNMENT: return "misaligned pointer";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_DEVICE: return "device query failed";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+int paged_attention_plan(const pa_dims* dims, size_t workspace_bytes, const pa_opts* opts,
+                         pa_plan* plan) {
+  if (plan == nullptr) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
+  pa_plan p;
+  const int st = make_plan(dims, decode_shape(dims), workspace_bytes, opts, false, &p);
+  if (st) return st;
+  *plan = p;
+  return ok();
+}
+
+size_t paged_attention_workspace_bytes(const pa_dims* dims, const pa_opts* opts) {
+  pa_plan p;
+  if (!dims || make_plan(dims, decode_shape(dims), 0, opts, true, &p)) return 0;
+  return p.workspace_bytes;
+}
+
+int paged_attention_decode(void* out, const void* query, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, float scale, int32_t block_size,
+                           const float* alibi_slopes, pa_stream_t stream, const pa_dims* dims,
+                           void* workspace, size_t workspace_bytes, const pa_opts* opts) {
+  if (dims == nullptr) return fail(PA_ERR_INVALID_ARG, "dims is NULL");
+  return run_attention(out, query, key_cache, value_cache, block_tables, context_lens, nullptr,
+                       decode_shape(dims), scale, block_size, alibi_slopes, stream, dims,
+                       workspace, workspace_bytes, opts);
+}
+
+static CallShape prefill_shape(int32_t num_query_tokens, int32_t max_query_len) {
+  CallShape c;
+  c.multi = true;
+  c.rows = num_query_tokens;
+  c.max_new = max_query_len;
+  return c;
+}
+
+int paged_attention_prefill_plan(const pa_dims* dims, int32_t num_query_tokens,
+                                 int32_t max_query_len, size_t workspace_bytes,
+                                 const pa_opts* opts, pa_plan* plan) {
+  if (plan == nullptr) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
+  if (num_query_tokens < 0 || max_query_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "num_query_tokens %d, max_query_len %d", num_query_tokens,
+                max_query_len);
+  pa_plan p;
+  const int st = make_plan(dims, prefill_shape(num_query_tokens, max_query_len), workspace_bytes,
+                           opts, false, &p);
+  if (st) return st;
+  *plan = p;
+  return ok();
+}
+
+size_t paged_attention_prefill_workspace_bytes(const pa_dims* dims, int32_t num_query_tokens,
+                                               int32_t max_query_len, const pa_opts* opts) {
+  pa_plan p;
+  if (!dims || num_query_tokens < 0 || max_query_len < 0 ||
+      make_plan(dims, prefill_shape(num_query_tokens, max_query_len), 0, opts, true, &p))
+    return 0;
+  return p.workspace_bytes;
+}
+
+int paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* query_start_loc,
+                            int32_t num_query_tokens, int32_t max_query_len, float scale,
+                            int32_t block_size, const float* alibi_slopes, pa_stream_t stream,
+                            const pa_dims* dims, void* workspace, size_t workspace_bytes,
+                            const pa_opts* opts) {
+  if (dims == nullptr) return fail(PA_ERR_INVALID_ARG, "dims is NULL");
+  return run_attention(out, query, key_cache, value_cache, block_tables, context_lens,
+                       query_start_loc, prefill_shape(num_query_tokens, max_query_len), scale,
+                       block_size, alibi_slopes, stream, dims, workspace, workspace_bytes, opts);
 }
 
 // Shared checks of the two row-copy entry points.

@@ -130,40 +130,72 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const int r = lane & 15;
   const int j = lane >> 4;
 
-  const int kvh = blockIdx.x;
+  // ---- which query rows this workgroup owns ---------------------------------
+  // A row is a (new token i, query head g) pair of one sequence and kv head,
+  // numbered i * G + g; the workgroup owns NT * 16 consecutive rows.  Decode
+  // has one new token per sequence, so its rows are the group's G heads.
+  const int chunks = a.row_chunks;
+  const int kvh = blockIdx.x / chunks;
+  const int rc = blockIdx.x - kvh * chunks;
   const int seq = blockIdx.y;
   const int part = blockIdx.z;
   const int G = a.group;
   const int h0 = kvh * G;
   const bool single = a.num_partitions == 1;
+  int q_first = seq, n_new = 1;  // packed index of the sequence's first new token
+  if (a.query_start != nullptr) {
+    q_first = a.query_start[seq];
+    n_new = a.query_start[seq + 1] - q_first;
+  }
+  const int row_base = rc * NT * 16;
+  const int nrows = n_new * G;
+  if (row_base >= nrows) return;  // this sequence has fewer rows
 
   const int L = min(a.context_lens[seq], a.max_blocks_per_seq * BS);
-  const int tok0 = part * a.partition_blocks * BS;
   if (L <= 0) {
-    if (single) {
-      uint4* o = reinterpret_cast<uint4*>(a.out) + ((size_t)seq * a.num_heads + h0) * CH;
-      for (int i = threadIdx.x; i < G * CH; i += NTHREADS) o[i] = make_uint4(0, 0, 0, 0);
+    if (single) {  // no context: zero output rows
+      for (int idx = threadIdx.x; idx < NT * 16 * CH; idx += NTHREADS) {
+        const int rr = row_base + idx / CH;
+        if (rr < nrows) {
+          const int ti = rr / G;
+          reinterpret_cast<uint4*>(a.out)[((size_t)(q_first + ti) * a.num_heads + h0 + rr - ti * G) * CH +
+                                          idx % CH] = make_uint4(0, 0, 0, 0);
+        }
+      }
     }
     return;
   }
-  if (tok0 >= L) return;  // partition past this sequence's end: nothing to do
-  const int tok1 = min(L, tok0 + a.partition_blocks * BS);
+  // the owned rows see keys up to the position of the last owned new token
+  const int last_new = min(n_new, (row_base + NT * 16 + G - 1) / G) - 1;
+  const int kend = L - n_new + last_new + 1;
+  const int tok0 = part * a.partition_blocks * BS;
+  if (tok0 >= kend) return;  // partition past every owned row's keys: nothing to do
+  const int tok1 = min(kend, tok0 + a.partition_blocks * BS);
   const int tile0 = tok0 / TT;                     // first tile of the partition
   const int ntiles = (tok1 - tok0 + TT - 1) / TT;  // tiles holding its tokens
 
-  // ---- shared query load: the group's G rows, zero-padded to NT * 16 ------
+  // ---- shared query load: the owned rows, zero-padded to NT * 16 ----------
   __shared__ uint4 q_lds[NT * 16 * CH];
-  {
-    const uint4* qg = reinterpret_cast<const uint4*>(a.q) + ((size_t)seq * a.num_heads + h0) * CH;
-    for (int i = threadIdx.x; i < NT * 16 * CH; i += NTHREADS)
-      q_lds[i] = (i < G * CH) ? qg[i] : make_uint4(0, 0, 0, 0);
+  for (int idx = threadIdx.x; idx < NT * 16 * CH; idx += NTHREADS) {
+    const int rr = row_base + idx / CH;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (rr < nrows) {
+      const int ti = rr / G;
+      v = reinterpret_cast<const uint4*>(a.q)[((size_t)(q_first + ti) * a.num_heads + h0 + rr - ti * G) *
+                                                  CH + idx % CH];
+    }
+    q_lds[idx] = v;
   }
   __syncthreads();
-  const int g = tile * 16 + r;  // this lane's head within the group
+  const int row = row_base + tile * 16 + r;  // this lane's row
+  const bool row_ok = row < nrows;
+  const int ti = row / G;                    // its new token
+  const int g = row - ti * G;                // its query head within the group
+  const int pos = row_ok ? L - n_new + ti : -1;  // its position: keys 0 .. pos are visible
   uint4 qb[NK];
 #pragma unroll
-  for (int i = 0; i < NK; ++i) qb[i] = q_lds[g * CH + 4 * i + j];
-  const float slope = (a.alibi != nullptr && g < G) ? a.alibi[h0 + g] * kLog2e : 0.f;
+  for (int i = 0; i < NK; ++i) qb[i] = q_lds[(tile * 16 + r) * CH + 4 * i + j];
+  const float slope = (a.alibi != nullptr && row_ok) ? a.alibi[h0 + g] * kLog2e : 0.f;
 
   float m = kNegBig, lsum = 0.f;
   f32x4_t acc[EPL];
@@ -180,7 +212,6 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const uint32_t k_lane = (uint32_t)(r * D + j * 8) * ES;          // step-0 K chunk
   const uint32_t v_lane = (uint32_t)((4 * j) * D + r * EPL) * ES;  // load-0 V slice
   const uint32_t tile_bytes = (uint32_t)TT * D * ES;
-  const int qpos = L - 1;
 
   // One 16-row tile's K and V in registers, as stored in the cache.
   struct Tile {
@@ -221,8 +252,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int t = 4 * j + v;
-      const float z = fmaf(s[v], a.scale_log2, slope * (float)(tb + t - qpos));
-      x[v] = t < valid ? z : kNegBig;
+      const float z = fmaf(s[v], a.scale_log2, slope * (float)(tb + t - pos));
+      x[v] = (t < valid && tb + t <= pos) ? z : kNegBig;
     }
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, shfl_xor(mx, 16));
@@ -304,11 +335,11 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   }
 
   // ---- finalise ---------------------------------------------------------------
-  if (tg != 0 || g >= G) return;
+  if (tg != 0 || !row_ok) return;
   const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
-  const size_t row = (size_t)seq * a.num_heads + h0 + g;
+  const size_t orow_idx = (size_t)(q_first + ti) * a.num_heads + h0 + g;
   if (single) {
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + row * D;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + orow_idx * D;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       uint32_t wv[EPL / 2];
@@ -320,7 +351,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       *reinterpret_cast<VT*>(orow + EPL * (4 * j + v)) = o;
     }
   } else {
-    const size_t slot = row * a.num_partitions + part;
+    const size_t slot = orow_idx * a.num_partitions + part;
     float* orow = a.ws_o + slot * D;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -338,7 +369,7 @@ namespace {
 
 template <typename Fmt, int D, int NT, int TG, bool KV8>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.num_kv_heads, a.num_seqs, a.num_partitions);
+  dim3 grid(a.num_kv_heads * a.row_chunks, a.num_seqs, a.num_partitions);
   decode_mfma_kernel<Fmt, D, NT, TG, KV8><<<grid, NT * TG * 64, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -347,6 +378,9 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
 // 4 waves where possible (3 x 2 = 6 for 48-head groups).
 template <typename Fmt, int D, bool KV8>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
+  // multi-query: 4 row tiles (64 query rows) per workgroup, one wave each,
+  // all walking the same keys
+  if (a.query_start != nullptr) return launch_t<Fmt, D, kPrefillRowTiles, 1, KV8>(a, s);
   switch (mfma_head_tiles(a.group)) {
     case 1: return launch_t<Fmt, D, 1, 4, KV8>(a, s);
     case 2: return launch_t<Fmt, D, 2, 2, KV8>(a, s);

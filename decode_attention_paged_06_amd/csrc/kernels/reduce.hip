@@ -9,8 +9,10 @@
 //   o_p  its softmax-normalised output (fp32).
 // The full result is the exact merge
 //   M = max_p m_p,  w_p = l_p * exp2(m_p - M),  out = sum_p w_p o_p / sum_p w_p
-// over the partitions that hold tokens of s (p < ceil(L_s / partition_size)).
-// One wave per (head, sequence); lane k owns D/64 output elements.
+// over the partitions that hold keys the row sees (p < ceil(visible /
+// partition_size), visible = L_s for decode, position + 1 for a new token of a
+// multi-query call).  One wave per (head, sequence, new token); lane k owns
+// D/64 output elements.
 #include "../launch.h"
 #include "device_common.h"
 
@@ -22,8 +24,15 @@ __global__ __launch_bounds__(64) void partition_reduce_kernel(const DecodeArgs a
   static_assert(PER == 1 || PER == 2, "head size 64 or 128");
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
+  const int i = blockIdx.z;  // new token of the sequence (0 for decode)
   const int lane = threadIdx.x;
-  const size_t row = (size_t)seq * a.num_heads + h;
+  int q_first = seq, n_new = 1;
+  if (a.query_start != nullptr) {
+    q_first = a.query_start[seq];
+    n_new = a.query_start[seq + 1] - q_first;
+  }
+  if (i >= n_new) return;
+  const size_t row = (size_t)(q_first + i) * a.num_heads + h;
   uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + row * D + lane * PER;
 
   const int L = min(a.context_lens[seq], a.max_blocks_per_seq * a.block_size);
@@ -32,8 +41,10 @@ __global__ __launch_bounds__(64) void partition_reduce_kernel(const DecodeArgs a
     else *orow = 0;
     return;
   }
+  // partitions holding the keys this row sees (0 .. its position)
   const int ptok = a.partition_blocks * a.block_size;
-  const int nact = min(a.num_partitions, (L + ptok - 1) / ptok);
+  const int visible = L - n_new + i + 1;
+  const int nact = min(a.num_partitions, (visible + ptok - 1) / ptok);
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + row * a.num_partitions;
   const float* o = a.ws_o + row * a.num_partitions * D + lane * PER;
 
@@ -61,7 +72,7 @@ __global__ __launch_bounds__(64) void partition_reduce_kernel(const DecodeArgs a
 }
 
 hipError_t launch_partition_reduce(const DecodeArgs& a, int dtype, int head_size, hipStream_t s) {
-  dim3 grid(a.num_heads, a.num_seqs);
+  dim3 grid(a.num_heads, a.num_seqs, a.max_new_tokens);
   if (dtype == 0) {
     if (head_size == 64) partition_reduce_kernel<F16, 64><<<grid, 64, 0, s>>>(a);
     else partition_reduce_kernel<F16, 128><<<grid, 64, 0, s>>>(a);

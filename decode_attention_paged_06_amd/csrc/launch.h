@@ -37,7 +37,18 @@ struct DecodeArgs {
   int32_t block_size;           // tokens per cache block (a power of two, 8..256)
   int32_t block_shift;          // log2(block_size)
   float v_scale;                // multiplies the values (1 for 16-bit caches)
+  // Multi-query (prefill) calls: sequence s's new tokens are packed rows
+  // query_start[s] .. query_start[s+1]-1 of q/out and are its last
+  // query_start[s+1]-query_start[s] context tokens.  nullptr = decode (one new
+  // token per sequence, row s).
+  const int32_t* query_start;
+  int32_t max_new_tokens;       // bound on new tokens per sequence (1 for decode)
+  int32_t row_chunks;           // workgroups per (sequence, kv head) over the query rows
 };
+
+// Head tiles of the MFMA decode workgroup for a group size, and the query-row
+// tiles of a multi-query workgroup.
+constexpr int kPrefillRowTiles = 4;
 
 // Query heads per VALU workgroup for a group size (heads that share a kv head
 // are processed in chunks of this many; larger groups use several chunks).

@@ -100,6 +100,53 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
     return out
 
 
+def make_prefill_dims(query: torch.Tensor, key_cache: torch.Tensor, block_tables: torch.Tensor,
+                      num_seqs: int, k_scale: float = 1.0, v_scale: float = 1.0) -> PaDims:
+    dims = make_dims(query, key_cache, block_tables, k_scale, v_scale)
+    dims.num_seqs = int(num_seqs)
+    return dims
+
+
+def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                            value_cache: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                            max_query_len: int, scale: float, block_size: int,
+                            alibi_slopes: Optional[torch.Tensor] = None, stream=None,
+                            workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
+                            k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+    """Enqueue causal multi-query attention for packed new tokens; returns ``out``."""
+    _require(out, "out", query.dtype)
+    _require(query, "query", query.dtype)
+    kv_dtype = torch.float8_e4m3fn if key_cache.dtype == torch.float8_e4m3fn else query.dtype
+    _require(key_cache, "key_cache", kv_dtype)
+    _require(value_cache, "value_cache", kv_dtype)
+    _require(block_tables, "block_tables", torch.int32)
+    _require(context_lens, "context_lens", torch.int32)
+    _require(query_start_loc, "query_start_loc", torch.int32)
+    if alibi_slopes is not None:
+        _require(alibi_slopes, "alibi_slopes", torch.float32)
+    S = context_lens.shape[0]
+    T = query.shape[0]
+    dims = make_prefill_dims(query, key_cache, block_tables, S, k_scale, v_scale)
+    opts = make_opts(partition_size, "auto")
+    if workspace is None:
+        nbytes = int(lib().paged_attention_prefill_workspace_bytes(
+            ctypes.byref(dims), T, int(max_query_len), ctypes.byref(opts)))
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=query.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _require(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().paged_attention_prefill(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), query_start_loc.data_ptr(), T,
+        int(max_query_len), float(scale), int(block_size),
+        alibi_slopes.data_ptr() if alibi_slopes is not None else None, _stream_ptr(stream),
+        ctypes.byref(dims), ws_ptr, ws_bytes, ctypes.byref(opts)))
+    return out
+
+
 def gather_cached_kv(key_out: torch.Tensor, value_out: torch.Tensor, key_cache: torch.Tensor,
                      value_cache: torch.Tensor, slot_mapping: torch.Tensor, block_size: int,
                      stream=None):
@@ -133,4 +180,4 @@ def paged_kv_cache_write(key_cache: torch.Tensor, value_cache: torch.Tensor, key
 
 
 __all__ = ["paged_attention_decode", "paged_attention_plan", "paged_attention_workspace_bytes",
-           "gather_cached_kv", "paged_kv_cache_write", "make_dims", "make_opts", "_lib"]
+           "paged_attention_prefill", "make_prefill_dims", "gather_cached_kv", "paged_kv_cache_write", "make_dims", "make_opts", "_lib"]

@@ -176,6 +176,47 @@ int paged_attention_plan(const pa_dims* dims, size_t workspace_bytes, const pa_o
                          pa_plan* plan);
 
 /*
+ * paged_attention_prefill -- causal multi-query attention over the paged
+ * cache: a chunk of new tokens per sequence attends to the cached prefix and
+ * to itself (the pages note the FlashAttention cache call serves prefill with
+ * and without a cached prefix, vLLM PR #2744 discussion).
+ *
+ * Sequence s owns the packed query rows query_start_loc[s] ..
+ * query_start_loc[s+1] - 1 (n_s rows, n_s <= context_lens[s]); these are its
+ * last n_s context tokens, whose K/V are already in the cache (written with
+ * paged_kv_cache_write).  New token i of s sits at position
+ * p = context_lens[s] - n_s + i and attends to positions 0 .. p:
+ *
+ *   out[row, h, :] = sum_{t <= p} softmax_t(scale * q[row, h].K_s[kvh, t]
+ *                                          + alibi_h * (t - p)) V_s[kvh, t, :]
+ *
+ * With n_s = 1 for every sequence this is paged_attention_decode.
+ *
+ * query, out        [num_query_tokens, num_heads, head_size]  dtype
+ * query_start_loc   [num_seqs + 1] int32, non-decreasing, [0] = 0,
+ *                   [num_seqs] = num_query_tokens (device memory)
+ * max_query_len     host-side bound on n_s (sizes the grid); 1 .. 65535
+ * Everything else as paged_attention_decode (dims->num_seqs sequences).  The
+ * matrix-core engine computes it (PA_ENGINE_VALU is rejected).  Device-side
+ * preconditions: n_s <= max_query_len and n_s <= context_lens[s].
+ */
+int paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* query_start_loc,
+                            int32_t num_query_tokens, int32_t max_query_len, float scale,
+                            int32_t block_size, const float* alibi_slopes, pa_stream_t stream,
+                            const pa_dims* dims, void* workspace, size_t workspace_bytes,
+                            const pa_opts* opts);
+
+/* Workspace and plan of a paged_attention_prefill call (host only; see the
+ * decode versions). */
+size_t paged_attention_prefill_workspace_bytes(const pa_dims* dims, int32_t num_query_tokens,
+                                               int32_t max_query_len, const pa_opts* opts);
+int paged_attention_prefill_plan(const pa_dims* dims, int32_t num_query_tokens,
+                                 int32_t max_query_len, size_t workspace_bytes,
+                                 const pa_opts* opts, pa_plan* plan);
+
+/*
  * gather_cached_kv -- copy cached K/V rows into contiguous tensors, bit for
  * bit (the operation benchmarked on vLLM PR #29, whose parameters are
  * num_tokens, num_heads, head_size, block_size and num_blocks).

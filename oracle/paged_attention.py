@@ -305,3 +305,48 @@ def kv_cache_write(key_cache_raw, value_cache_raw, key_raw, value_raw, slot_mapp
         kc[slot // block_size, :, slot % block_size, :] = k[i]
         vc[slot // block_size, :, slot % block_size, :] = v[i]
     return kc, vc
+
+
+def query_position(L: int, n: int, i: int) -> int:
+    """Position of new token i when the last n of L context tokens are new."""
+    return L - n + i
+
+
+def paged_prefill(query, key_cache, value_cache, block_tables, context_lens, query_start,
+                  scale: float, block_size: int, alibi_slopes=None, dtype: Optional[str] = None,
+                  k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """Causal multi-query attention over the paged cache, float64 [T, Hq, D].
+
+    Sequence s owns query rows query_start[s] .. query_start[s+1] - 1 (T rows in
+    all); they are its last n_s = query_start[s+1] - query_start[s] context
+    tokens, already stored in the cache (reading taken for running the
+    FlashAttention cache call on prefill chunks, vLLM PR #2744 discussion).
+    Query i of s sits at position p = L_s - n_s + i and attends to positions
+    0 .. p; the ALiBi bias is slope * (t - p).  With n_s = 1 this is exactly
+    paged_decode.
+    """
+    q_all = np.asarray(query)
+    T, Hq, D = q_all.shape
+    Hkv = np.asarray(key_cache).shape[1]
+    tables = np.asarray(block_tables)
+    lens = np.asarray(context_lens)
+    qs = np.asarray(query_start)
+    slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float32)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for s in range(len(lens)):
+        L = int(lens[s])
+        first, n = int(qs[s]), int(qs[s + 1]) - int(qs[s])
+        if n <= 0 or L <= 0:
+            continue
+        if n > L:
+            raise ValueError("a sequence has more new tokens than context")
+        K = _as_f64(sequence_kv(key_cache, tables[s], L, block_size), dtype) * float(np.float32(k_scale))
+        V = _as_f64(sequence_kv(value_cache, tables[s], L, block_size), dtype) * float(np.float32(v_scale))
+        for i in range(n):
+            p = query_position(L, n, i)
+            q = _as_f64(q_all[first + i], dtype)
+            for h in range(Hq):
+                kvh = kv_head_of(h, Hq, Hkv)
+                bias = None if slopes is None else alibi_bias(float(slopes[h]), p + 1)
+                out[first + i, h] = attend(q[h], K[kvh, :p + 1], V[kvh, :p + 1], scale, bias)
+    return out

@@ -405,10 +405,95 @@ def pin_fp8_cache_scales():
     assert np.isfinite(got).all() and np.array_equal(got, ref)
 
 
+def _brute_prefill(q, kc, vc, tables, lens, qs, scale, BS, slopes):
+    """Pure-Python causal attention: query i of s sees positions 0 .. L - n + i."""
+    T, Hq, D = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(kc[0])
+    head_mapping = [k for k in range(Hkv) for _ in range(Hq // Hkv)]
+    out = [[[0.0] * D for _ in range(Hq)] for _ in range(T)]
+    for s in range(len(lens)):
+        L, n = lens[s], qs[s + 1] - qs[s]
+        for i in range(n):
+            p = L - n + i
+            for h in range(Hq):
+                kvh = head_mapping[h]
+                zs = []
+                for t in range(p + 1):
+                    blk, off = tables[s][t // BS], t % BS
+                    z = scale * math.fsum(q[qs[s] + i][h][d] * kc[blk][kvh][off][d] for d in range(D))
+                    if slopes is not None:
+                        z += slopes[h] * (t - p)
+                    zs.append(z)
+                mx = max(zs)
+                w = [math.exp(z - mx) for z in zs]
+                den = math.fsum(w)
+                for d in range(D):
+                    out[qs[s] + i][h][d] = math.fsum(
+                        w[t] * vc[tables[s][t // BS]][kvh][t % BS][d] for t in range(p + 1)) / den
+    return np.array(out)
+
+
+def _prefill_case(seed=13, lens=(5, 9, 1, 12), news=(3, 9, 1, 4), alibi=True, dtype="bf16"):
+    inp = decode_inputs(num_seqs=len(lens), num_heads=6, num_kv_heads=2, head_size=8,
+                        block_size=4, dtype=dtype, seed=seed, context_lens=list(lens),
+                        alibi=alibi, poison=True)
+    qs = np.concatenate([[0], np.cumsum(news)]).astype(np.int64)
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(int(qs[-1]), 6, 8, generator=g).to(inp.query.dtype)
+    return inp, q, qs
+
+
+def pin_prefill_brute_force():
+    inp, q, qs = _prefill_case()
+    f = lambda t: ora.to_float64(raw_u16(t), "bf16").tolist()   # noqa: E731
+    slopes = [float(x) for x in inp.alibi_slopes.numpy()]
+    ref = _brute_prefill(f(q), f(inp.key_cache), f(inp.value_cache), inp.block_tables.tolist(),
+                         inp.context_lens.tolist(), qs.tolist(), inp.scale, 4, slopes)
+    got = ora.paged_prefill(raw_u16(q), raw_u16(inp.key_cache), raw_u16(inp.value_cache),
+                            inp.block_tables.numpy(), inp.context_lens.numpy(), qs, inp.scale, 4,
+                            inp.alibi_slopes.numpy(), dtype="bf16")
+    assert np.isfinite(got).all() and np.max(np.abs(got - ref)) <= 1e-12
+
+
+def pin_prefill_last_token_is_decode():
+    """Each sequence's last query row equals decode of that query over the whole context."""
+    inp, q, qs = _prefill_case(alibi=True)
+    got = ora.paged_prefill(raw_u16(q), raw_u16(inp.key_cache), raw_u16(inp.value_cache),
+                            inp.block_tables.numpy(), inp.context_lens.numpy(), qs, inp.scale, 4,
+                            inp.alibi_slopes.numpy(), dtype="bf16")
+    last = raw_u16(q)[qs[1:] - 1]
+    dec = ora.paged_decode(last, raw_u16(inp.key_cache), raw_u16(inp.value_cache),
+                           inp.block_tables.numpy(), inp.context_lens.numpy(), inp.scale, 4,
+                           inp.alibi_slopes.numpy(), dtype="bf16")
+    assert np.array_equal(got[qs[1:] - 1], dec)
+
+
+def pin_prefill_dense_causal_library():
+    """Against SDPA with an explicit causal mask on dense K/V built by this test."""
+    import torch.nn.functional as F
+    rng = _rng(11)
+    lens, news = [20, 7, 33], [6, 7, 1]
+    Hq, Hkv, D, BS = 4, 2, 8, 8
+    kc, vc, tables, dk, dv, _ = _scatter_dense(rng, lens, Hkv, D, BS)
+    qs = np.concatenate([[0], np.cumsum(news)])
+    q = rng.standard_normal((int(qs[-1]), Hq, D))
+    got = ora.paged_prefill(q, kc, vc, tables, np.array(lens), qs, 0.4, BS)
+    for s, (L, n) in enumerate(zip(lens, news)):
+        idx = torch.tensor([h // (Hq // Hkv) for h in range(Hq)])
+        K = torch.from_numpy(dk[s])[idx]
+        V = torch.from_numpy(dv[s])[idx]
+        Q = torch.from_numpy(q[qs[s]:qs[s] + n]).permute(1, 0, 2)       # [Hq, n, D]
+        pos = torch.arange(L - n, L)[:, None]
+        mask = torch.where(torch.arange(L)[None, :] <= pos, 0.0, float("-inf")).to(torch.float64)
+        ref = F.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=0.4).permute(1, 0, 2)
+        assert np.max(np.abs(got[qs[s]:qs[s] + n] - ref.numpy())) <= 1e-12
+
+
 PINS = [
     pin_brute_force, pin_dense_library, pin_gather_by_construction,
     pin_sequence_kv_by_construction, pin_block_permutation, pin_context_one,
     pin_identical_keys_mean, pin_identical_keys_alibi, pin_needle, pin_gqa_equals_repeated_mha,
     pin_split_merge, pin_shift_and_linearity, pin_empty_context, pin_poison_ignored,
     pin_storage_formats, pin_cache_write_round_trip, pin_fp8_format, pin_fp8_cache_scales,
+    pin_prefill_brute_force, pin_prefill_last_token_is_decode, pin_prefill_dense_causal_library,
 ]

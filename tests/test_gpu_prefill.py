@@ -1,0 +1,83 @@
+"""GPU parity of the causal multi-query (prefill) call against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_paged_06_amd import paged_attention_decode, paged_attention_prefill
+from gpu_util import TOL, compare, device
+from workloads import prefill_inputs, raw_bits, raw_u16
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(inp, q, qs, max_q, partition_size=0):
+    out = torch.full_like(q, float("nan"))
+    paged_attention_prefill(out, q, inp.key_cache, inp.value_cache, inp.block_tables,
+                            inp.context_lens, qs, max_q, inp.scale, inp.block_size,
+                            inp.alibi_slopes, partition_size=partition_size,
+                            k_scale=inp.k_scale, v_scale=inp.v_scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def ref_prefill(inp, q, qs):
+    slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.cpu().numpy()
+    return oracle.paged_prefill(raw_u16(q), raw_bits(inp.key_cache), raw_bits(inp.value_cache),
+                                inp.block_tables.cpu().numpy(), inp.context_lens.cpu().numpy(),
+                                qs.cpu().numpy(), inp.scale, inp.block_size, slopes,
+                                dtype=inp.dtype, k_scale=inp.k_scale, v_scale=inp.v_scale)
+
+
+CASES = [
+    # (name, heads, kv heads, head size, dtype, block, lengths, new tokens, alibi, kv dtype)
+    ("gqa-prefix", 16, 2, 128, "bf16", 16, [40, 300, 17, 129], [7, 64, 17, 1], True, None),
+    ("mha-fresh", 4, 4, 64, "f16", 16, [33, 70, 5], [33, 70, 5], False, None),
+    ("mqa-48", 48, 1, 128, "f16", 16, [100, 260], [20, 3], True, None),
+    ("gqa-block8", 16, 2, 128, "bf16", 8, [50, 9, 200], [50, 2, 31], True, None),
+    ("gqa-block64", 8, 1, 64, "f16", 64, [65, 300], [1, 128], False, None),
+    ("fp8-cache", 16, 2, 128, "bf16", 16, [90, 257], [45, 100], True, "fp8"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_parity(case):
+    dev = device()
+    name, Hq, Hkv, D, dtype, BS, lens, news, alibi, kvd = case
+    inp, q, qs, max_q = prefill_inputs(new_tokens=news, seed=len(name) + sum(news), device=dev,
+                                       num_seqs=len(lens), num_heads=Hq, num_kv_heads=Hkv,
+                                       head_size=D, block_size=BS, dtype=dtype,
+                                       context_lens=lens, alibi=alibi, poison=True, kv_dtype=kvd)
+    ref = ref_prefill(inp, q, qs)
+    for ps in (-1, 0, max(BS, 64)):
+        compare(run_prefill(inp, q, qs, max_q, ps), ref, dtype, what=f"{name} partition={ps}")
+
+
+def test_prefill_one_token_matches_decode():
+    dev = device()
+    lens = [1, 50, 300, 1000]
+    inp, q, qs, max_q = prefill_inputs(new_tokens=[1] * 4, seed=5, device=dev, num_seqs=4,
+                                       num_heads=64, num_kv_heads=8, head_size=128,
+                                       block_size=16, dtype="bf16", context_lens=lens,
+                                       alibi=True, poison=True)
+    a = run_prefill(inp, q, qs, max_q)
+    b = torch.empty_like(q)
+    paged_attention_decode(b, q, inp.key_cache, inp.value_cache, inp.block_tables,
+                           inp.context_lens, inp.scale, 16, inp.alibi_slopes)
+    torch.cuda.synchronize()
+    assert float((a.float() - b.float()).abs().max()) <= TOL["bf16"]
+    compare(a, ref_prefill(inp, q, qs), "bf16", what="prefill n=1")
+
+
+def test_prefill_empty_sequences_and_chunk():
+    """Sequences with no new tokens produce no rows; a long chunk spans many row tiles."""
+    dev = device()
+    lens = [64, 2000, 10, 700]
+    news = [0, 300, 0, 77]
+    inp, q, qs, max_q = prefill_inputs(new_tokens=news, seed=9, device=dev, num_seqs=4,
+                                       num_heads=32, num_kv_heads=4, head_size=128,
+                                       block_size=16, dtype="bf16", context_lens=lens,
+                                       poison=True)
+    ref = ref_prefill(inp, q, qs)
+    for ps in (0, 256):
+        compare(run_prefill(inp, q, qs, max_q, ps), ref, "bf16", what=f"chunk partition={ps}")

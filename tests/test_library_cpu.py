@@ -163,6 +163,28 @@ def test_fp8_cache_validation(L):
     assert g(None, None, None, None, None, 0, 8, 16, 16, 10, 2, None) == OK
 
 
+def test_prefill_validation(L):
+    d = dims(S=4)
+    o = PaOpts(-1, 1, 256, 0)      # the VALU engine cannot run multi-query calls
+    pf = L.paged_attention_prefill
+    args = lambda **k: (k.get("out", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, k.get("qs", FAKE),  # noqa: E731
+                        k.get("T", 100), k.get("maxq", 40), ctypes.c_float(0.1), 16, None, None,
+                        ctypes.byref(d), None, 0, ctypes.byref(k.get("opts", PaOpts(-1, 0, 256, 0))))
+    assert pf(*args(opts=o)) == UNSUPPORTED
+    assert pf(*args(qs=None)) == INVALID
+    assert pf(*args(T=-1)) == INVALID
+    assert pf(*args(maxq=70000)) == INVALID
+    assert pf(*args(qs=FAKE + 2)) == ALIGN
+    assert pf(*args(T=0)) == OK and pf(*args(maxq=0)) == OK
+    p = PaPlan()
+    assert L.paged_attention_prefill_plan(ctypes.byref(dims(S=1, MAXB=256)), 512, 512, 1 << 40,
+                                          ctypes.byref(PaOpts(0, 0, 256, 0)), ctypes.byref(p)) == OK
+    assert p.engine == 2
+    rows = 512 * 64 * p.num_partitions
+    assert p.workspace_bytes == (0 if p.num_partitions == 1 else
+                                 ((rows * 128 * 4 + 255) // 256) * 256 + rows * 8)
+
+
 def test_plan_rejects_group_above_limit(L):
     assert plan(L, dims(Hq=128, Hkv=1))[0] == UNSUPPORTED
 

@@ -11,7 +11,8 @@ from oracle_pins import PINS
 
 _orig = {name: getattr(ora, name) for name in
          ("kv_head_of", "sequence_kv", "alibi_bias", "attend", "merge_partitions",
-          "gather_cached_kv", "to_float64", "kv_cache_write", "fp8_to_float64")}
+          "gather_cached_kv", "to_float64", "kv_cache_write", "fp8_to_float64",
+          "query_position")}
 
 
 def _kv_head_mod(h, Hq, Hkv):
@@ -110,6 +111,14 @@ def _fp8_no_subnormals(raw):
     return np.where((np.asarray(raw) & 0x78) == 0, 0.0, v)
 
 
+def _position_off_by_one(L, n, i):
+    return max(L - n + i - 1, 0)
+
+
+def _position_first_token(L, n, i):
+    return L - 1    # every new token sees the whole context (no causal mask)
+
+
 MUTANTS = {
     "head_mapping_modulo": ("kv_head_of", _kv_head_mod),
     "drop_last_token": ("sequence_kv", _seq_drop_last),
@@ -129,6 +138,8 @@ MUTANTS = {
     "cache_write_k_v_swapped": ("kv_cache_write", _write_kv_swapped),
     "fp8_exponent_bias_8": ("fp8_to_float64", _fp8_bias8),
     "fp8_subnormals_flushed": ("fp8_to_float64", _fp8_no_subnormals),
+    "prefill_position_off_by_one": ("query_position", _position_off_by_one),
+    "prefill_not_causal": ("query_position", _position_first_token),
 }
 
 

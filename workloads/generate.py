@@ -228,3 +228,22 @@ def raw_bits(t: torch.Tensor) -> np.ndarray:
     if t.element_size() == 1:
         return t.detach().contiguous().cpu().view(torch.uint8).numpy()
     return raw_u16(t)
+
+
+def prefill_inputs(*, new_tokens, seed: int, device: Union[str, torch.device] = "cpu",
+                   **decode_kwargs):
+    """A multi-query batch: decode_inputs for the caches plus packed new-token queries.
+
+    new_tokens gives n_s per sequence (each <= its context length): the last
+    n_s context tokens of sequence s are its new tokens.  Returns
+    (inputs, query [T, Hq, D], query_start [S + 1] int32, max_query_len).
+    """
+    inp = decode_inputs(seed=seed, device=device, **decode_kwargs)
+    news = [int(n) for n in new_tokens]
+    lens = inp.context_lens.cpu().tolist()
+    assert len(news) == len(lens) and all(0 <= n <= L for n, L in zip(news, lens))
+    starts = torch.tensor([0] + list(np.cumsum(news)), dtype=torch.int32)
+    g = torch.Generator(device=torch.device(device)).manual_seed(seed + 2)
+    q = _randn((int(starts[-1]), inp.query.shape[1], inp.query.shape[2]), inp.dtype, g,
+               torch.device(device))
+    return inp, q, starts.to(device), max(news + [1])
