@@ -30,8 +30,12 @@ SOURCES = [
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}"]
-# Packed-fp32 VALU forms are disabled for all device code.
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed-fp32 VALU forms are disabled for all device code.  MFMA results stay
+# in ordinary VGPRs: the decode loop rescales its P.V accumulators with VALU
+# multiplies every tile, and accumulators kept in AGPRs would need a copy to
+# VGPRs and back around each rescale.
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc() -> str:

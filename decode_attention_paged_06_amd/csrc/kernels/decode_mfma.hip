@@ -40,7 +40,7 @@
 // staging of K or V.
 //
 // Softmax: fp32 online softmax in log2 units; the running max of a head is
-// shared by the 4 lane groups j (two swizzles per block), each lane keeps a
+// shared by the 4 lane groups j (two lane swaps per tile), each lane keeps a
 // partial sum of its own rounded p values, and the accumulator rescale is
 // skipped when no lane's max moved.  P is rounded to the storage type before
 // the P.V product (the matrix cores take 16-bit operands); the sum l uses the
@@ -93,13 +93,11 @@ struct VRow<8> {
   static __device__ __forceinline__ uint32_t word(const T& v, int w) {
     return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
   }
-  static __device__ __forceinline__ T zero() { return make_uint4(0, 0, 0, 0); }
 };
 template <>
 struct VRow<4> {
   using T = uint2;
   static __device__ __forceinline__ uint32_t word(const T& v, int w) { return w == 0 ? v.x : v.y; }
-  static __device__ __forceinline__ T zero() { return make_uint2(0, 0); }
 };
 
 template <typename Fmt, int D, int NT, int TG, bool KV8>
@@ -121,6 +119,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   using KRaw = typename KS::Raw8;                // 8 cached K elements as loaded
   using VRaw = typename std::conditional<EPL == 8, typename KS::Raw8, typename KS::Raw4>::type;
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr int kDepth = 2;  // register tiles in the load pipeline
 
   constexpr int NTHREADS = NT * TG * 64;
   const int lane = threadIdx.x & 63;
@@ -191,7 +190,13 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const bool row_ok = row < nrows;
   const int ti = row / G;                    // its new token
   const int g = row - ti * G;                // its query head within the group
-  const int pos = row_ok ? L - n_new + ti : -1;  // its position: keys 0 .. pos are visible
+  // its position: keys 0 .. pos are visible (padding rows, past the last new
+  // token, get a position past L; their results are never stored)
+  const int pos = L - n_new + ti;
+  // the lowest position among the wave's 16 rows (wave-uniform): tiles that
+  // end at or before it, and are full, need no masking
+  const int pos_lo = L - n_new + (row_base + tile * 16) / G;
+  const bool has_alibi = a.alibi != nullptr;
   uint4 qb[NK];
 #pragma unroll
   for (int i = 0; i < NK; ++i) qb[i] = q_lds[(tile * 16 + r) * CH + 4 * i + j];
@@ -211,19 +216,26 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
   const uint32_t k_lane = (uint32_t)(r * D + j * 8) * ES;          // step-0 K chunk
   const uint32_t v_lane = (uint32_t)((4 * j) * D + r * EPL) * ES;  // load-0 V slice
-  const uint32_t tile_bytes = (uint32_t)TT * D * ES;
 
   // One 16-row tile's K and V in registers, as stored in the cache.
   struct Tile {
     KRaw k[NK];
     VRaw v[4];
   };
-  auto load = [&](Tile& T, int u) {  // u: tile index within the partition
+  // u: tile index within the partition; blk: its physical block (the table
+  // entry is read one tile ahead of the load that needs it, so the scalar
+  // load's latency hides behind a tile's processing).  The buffer bound is
+  // the tile's valid rows: rows past the context end (which may hold
+  // anything, NaN included) read back as zeros, and a tile past the end of
+  // the partition (u >= ntiles) reads nothing at all.  Every pipeline step
+  // thus issues the same loads, which keeps the wait counts exact.
+  auto block_of = [&](int u) { return table[(tile0 + min(u, ntiles - 1)) >> tpb_shift]; };
+  auto load = [&](Tile& T, int u, int blk) {
     const int ua = tile0 + u;
-    const size_t off = (size_t)table[ua >> tpb_shift] * bstride +
-                       (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
-    const rsrc_t rk = make_rsrc(kbase + off, tile_bytes);
-    const rsrc_t rv = make_rsrc(vbase + off, tile_bytes);
+    const size_t off = (size_t)blk * bstride + (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
+    const uint32_t bytes = u < ntiles ? (uint32_t)min(tok1 - ua * TT, TT) * (D * ES) : 0u;
+    const rsrc_t rk = make_rsrc(kbase + off, bytes);
+    const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
     for (int i = 0; i < NK; ++i)
       T.k[i] = KS::template load8<NT == 1>(rk, k_lane + 32u * ES * i);
@@ -249,15 +261,24 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 #pragma unroll
     for (int i = 0; i < NK; ++i) s = Mfma<Fmt>::qk(kk[i], qb[i], s);
     float x[4];
+    if (valid == 16 && tb + 15 <= pos_lo) {  // every row sees every key of the tile
+      if (has_alibi) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = 4 * j + v;
-      const float z = fmaf(s[v], a.scale_log2, slope * (float)(tb + t - pos));
-      x[v] = (t < valid && tb + t <= pos) ? z : kNegBig;
+        for (int v = 0; v < 4; ++v)
+          x[v] = fmaf(s[v], a.scale_log2, slope * (float)(tb + 4 * j + v - pos));
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[v] = s[v] * a.scale_log2;
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = 4 * j + v;
+        const float z = fmaf(s[v], a.scale_log2, slope * (float)(tb + t - pos));
+        x[v] = (t < valid && tb + t <= pos) ? z : kNegBig;
+      }
     }
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float mx = column_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
     const float mn = fmaxf(m, mx);
     const float alpha = fast_exp2(m - mn);
     m = mn;
@@ -268,12 +289,6 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     if (wave_any(alpha != 1.f)) {
 #pragma unroll
       for (int t = 0; t < EPL; ++t) acc[t] *= alpha;
-    }
-
-    if (valid < 16) {  // last tile of a sequence: slots past L may hold NaN
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * j + i >= valid) vv[i] = VR::zero();
     }
 
 #pragma unroll
@@ -287,25 +302,33 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     }
   };
 
-  // Software pipeline: the loads of the wave's next block are in flight while
-  // the current block is processed (two register tiles, used alternately).
-  Tile ta, tb2;
+  // Software pipeline of kDepth register tiles used in rotation: while one
+  // tile is processed, the loads of the wave's next kDepth - 1 tiles are in
+  // flight.
+  Tile buf[kDepth];
   int u = tg;
-  if (u < ntiles) load(ta, u);
-  while (u < ntiles) {
-    const int u1 = u + TG;
-    if (u1 < ntiles) load(tb2, u1);
-    process(ta, u);
-    if (u1 >= ntiles) break;
-    const int u2 = u1 + TG;
-    if (u2 < ntiles) load(ta, u2);
-    process(tb2, u1);
-    u = u2;
+  if (u < ntiles) {
+#pragma unroll
+    for (int k = 0; k + 1 < kDepth; ++k) load(buf[k], u + k * TG, block_of(u + k * TG));
+    int blk_next = block_of(u + (kDepth - 1) * TG);
+    bool more = true;
+    while (more) {
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k) {
+        if (more) {
+          const int uc = u + k * TG;
+          load(buf[(k + kDepth - 1) % kDepth], uc + (kDepth - 1) * TG, blk_next);
+          blk_next = block_of(uc + kDepth * TG);
+          process(buf[k], uc);
+          more = uc + TG < ntiles;
+        }
+      }
+      u += kDepth * TG;
+    }
   }
 
   // ---- complete the per-lane sums over the 4 lane groups -------------------
-  lsum += shfl_xor(lsum, 16);
-  lsum += shfl_xor(lsum, 32);
+  lsum = column_sum4(lsum);
 
   // ---- merge the token groups into group 0 (fixed order: deterministic) ----
   if constexpr (TG > 1) {

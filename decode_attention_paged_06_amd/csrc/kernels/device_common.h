@@ -97,6 +97,26 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
 }
 
+// Reductions over the four lanes l % 16 + 16 k (k = 0..3) with the gfx950
+// lane-swap instructions: permlane32_swap pairs lane l with l ^ 32 and
+// permlane16_swap pairs it with l ^ 16.  Plain VALU moves, no LDS round trip;
+// every lane of a group ends with the same value (max and + are commutative).
+__device__ __forceinline__ float xor32_pair_max(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xor16_pair_max(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float column_max4(float x) { return xor16_pair_max(xor32_pair_max(x)); }
+__device__ __forceinline__ float column_sum4(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 // True if any lane of the wave has `p` set.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
