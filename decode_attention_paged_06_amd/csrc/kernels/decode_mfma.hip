@@ -119,7 +119,22 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   using KRaw = typename KS::Raw8;                // 8 cached K elements as loaded
   using VRaw = typename std::conditional<EPL == 8, typename KS::Raw8, typename KS::Raw4>::type;
   constexpr float kLog2e = 1.4426950408889634f;
-  constexpr int kDepth = 2;  // register tiles in the load pipeline
+  constexpr int kDepth = 2;  // register tiles in the load pipeline (one wave per tile)
+  // With several head tiles the NT waves of a token group need the same K/V
+  // tile: it is staged once through a ring of kRing LDS slots instead.
+  constexpr bool STAGE = NT > 1;
+  constexpr int kRing = 4;
+  using KPiece = LdsPiece<KRaw>;
+  using VPiece = LdsPiece<VRaw>;
+  constexpr int kStageBytes = NK * KPiece::kBytes + 4 * VPiece::kBytes;
+  constexpr int kTransfers = NK * KPiece::kTransfers + 4 * VPiece::kTransfers;  // per tile
+  constexpr int kRingBytes = STAGE ? TG * kRing * kStageBytes : 0;
+  constexpr int kMergeBytes = TG > 1 ? NT * (EPL * 64 * 16 + 2 * 64 * 4) : 0;
+  constexpr int kWorkBytes = kRingBytes > kMergeBytes ? kRingBytes : (kMergeBytes > 16 ? kMergeBytes : 16);
+  // the ring during the tile loop, the token-group merge after it
+  __shared__ __align__(16) char work_lds[kWorkBytes];
+  constexpr int kTableWindow = 512;  // block-table entries held in LDS by the staged loop
+  __shared__ int tbl_lds[STAGE ? kTableWindow : 1];
 
   constexpr int NTHREADS = NT * TG * 64;
   const int lane = threadIdx.x & 63;
@@ -201,6 +216,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 #pragma unroll
   for (int i = 0; i < NK; ++i) qb[i] = q_lds[(tile * 16 + r) * CH + 4 * i + j];
   const float slope = (a.alibi != nullptr && row_ok) ? a.alibi[h0 + g] * kLog2e : 0.f;
+  // the slope's load completes here, before the tile loop's own memory traffic
+  asm volatile("" ::"v"(slope));
 
   float m = kNegBig, lsum = 0.f;
   f32x4_t acc[EPL];
@@ -302,29 +319,102 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     }
   };
 
-  // Software pipeline of kDepth register tiles used in rotation: while one
-  // tile is processed, the loads of the wave's next kDepth - 1 tiles are in
-  // flight.
-  Tile buf[kDepth];
-  int u = tg;
-  if (u < ntiles) {
+  if constexpr (!STAGE) {
+    // Software pipeline of kDepth register tiles used in rotation: while one
+    // tile is processed, the loads of the wave's next kDepth - 1 tiles are in
+    // flight.
+    Tile buf[kDepth];
+    int u = tg;
+    if (u < ntiles) {
 #pragma unroll
-    for (int k = 0; k + 1 < kDepth; ++k) load(buf[k], u + k * TG, block_of(u + k * TG));
-    int blk_next = block_of(u + (kDepth - 1) * TG);
-    bool more = true;
-    while (more) {
+      for (int k = 0; k + 1 < kDepth; ++k) load(buf[k], u + k * TG, block_of(u + k * TG));
+      int blk_next = block_of(u + (kDepth - 1) * TG);
+      bool more = true;
+      while (more) {
 #pragma unroll
-      for (int k = 0; k < kDepth; ++k) {
-        if (more) {
-          const int uc = u + k * TG;
-          load(buf[(k + kDepth - 1) % kDepth], uc + (kDepth - 1) * TG, blk_next);
-          blk_next = block_of(uc + kDepth * TG);
-          process(buf[k], uc);
-          more = uc + TG < ntiles;
+        for (int k = 0; k < kDepth; ++k) {
+          if (more) {
+            const int uc = u + k * TG;
+            load(buf[(k + kDepth - 1) % kDepth], uc + (kDepth - 1) * TG, blk_next);
+            blk_next = block_of(uc + kDepth * TG);
+            process(buf[k], uc);
+            more = uc + TG < ntiles;
+          }
         }
+        u += kDepth * TG;
       }
-      u += kDepth * TG;
     }
+  } else {
+    // LDS ring: the first wave of each token group copies tile tg + j TG into
+    // slot j % kRing, kRing - 1 tiles ahead; after its wait and a barrier
+    // every wave of the group reads the tile from the slot.  All waves of the
+    // workgroup run the same number of steps (every step has a barrier); a
+    // group's steps past its last tile copy nothing and process nothing.
+    //
+    // Block ids come from a window of the partition's table entries kept in
+    // LDS (the copies write memory the compiler cannot tell apart from the
+    // table, so the table is not read with scalar loads inside the loop).
+    // The window is refilled by all waves, between barriers, when the tiles
+    // being copied move past it.
+    const int b0 = tile0 >> tpb_shift;                          // first block of the partition
+    const int nblk = ((tile0 + ntiles - 1) >> tpb_shift) - b0 + 1;  // blocks it uses
+    auto fill_window = [&](int start) {
+      for (int i = threadIdx.x; i < kTableWindow; i += NTHREADS)
+        tbl_lds[i] = start + i < nblk ? table[b0 + start + i] : 0;
+    };
+    auto rel_block = [&](int u) { return ((tile0 + min(u, ntiles - 1)) >> tpb_shift) - b0; };
+    int win0 = 0;
+    fill_window(0);
+    __syncthreads();
+
+    char* ring = work_lds + tg * (kRing * kStageBytes);
+    const bool issuer = tile == 0;
+    auto copy = [&](int u, int slot) {
+      const int ua = tile0 + u;
+      const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[rel_block(u) - win0]);
+      const size_t off = (size_t)blk * bstride + (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
+      const uint32_t bytes = u < ntiles ? (uint32_t)min(tok1 - ua * TT, TT) * (D * ES) : 0u;
+      const rsrc_t rk = make_rsrc(kbase + off, bytes);
+      const rsrc_t rv = make_rsrc(vbase + off, bytes);
+      char* dst = ring + slot * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) KPiece::copy(rk, k_lane + 32u * ES * i, dst + i * KPiece::kBytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        VPiece::copy(rv, v_lane + (uint32_t)D * ES * i, dst + NK * KPiece::kBytes + i * VPiece::kBytes);
+    };
+    auto read = [&](Tile& T, int slot) {
+      const char* src = ring + slot * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) T.k[i] = KPiece::read(src + i * KPiece::kBytes, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T.v[i] = VPiece::read(src + NK * KPiece::kBytes + i * VPiece::kBytes, lane);
+    };
+    const int nsteps = (ntiles + TG - 1) / TG;
+    if (issuer) {
+#pragma unroll
+      for (int k = 0; k + 1 < kRing; ++k) copy(tg + k * TG, k);
+    }
+    for (int j = 0; j < nsteps; ++j) {
+      if (issuer) wait_vmcnt<kTransfers * (kRing - 2)>();  // tile j has landed
+      // the tiles copied in this step are (j + kRing - 1) TG + 0 .. TG - 1
+      const int first = (j + kRing - 1) * TG;
+      if (rel_block(first + TG - 1) >= win0 + kTableWindow) {  // same for every wave
+        lds_barrier();  // every issuer is done with the old window
+        win0 = rel_block(first);
+        fill_window(win0);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      }
+      lds_barrier();  // tile j is visible to every wave; slot (j - 1) % kRing is free
+      if (issuer) copy(tg + first, (j + kRing - 1) % kRing);
+      const int uc = tg + j * TG;
+      if (uc < ntiles) {
+        Tile T;
+        read(T, j % kRing);
+        process(T, uc);
+      }
+    }
+    if (issuer) wait_vmcnt<0>();  // the copies past the end have landed before the LDS is reused
   }
 
   // ---- complete the per-lane sums over the 4 lane groups -------------------
@@ -332,9 +422,9 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 
   // ---- merge the token groups into group 0 (fixed order: deterministic) ----
   if constexpr (TG > 1) {
-    __shared__ f32x4_t mrg_acc[NT][EPL][64];
-    __shared__ float mrg_m[NT][64];
-    __shared__ float mrg_l[NT][64];
+    auto mrg_acc = reinterpret_cast<f32x4_t(*)[EPL][64]>(work_lds);
+    auto mrg_m = reinterpret_cast<float(*)[64]>(work_lds + NT * EPL * 64 * 16);
+    auto mrg_l = reinterpret_cast<float(*)[64]>(work_lds + NT * EPL * 64 * 16 + NT * 64 * 4);
     for (int k = 1; k < TG; ++k) {
       __syncthreads();
       if (tg == k) {

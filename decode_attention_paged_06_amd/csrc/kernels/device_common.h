@@ -163,6 +163,97 @@ __device__ __forceinline__ uint32_t buffer_load_b32(rsrc_t r, uint32_t off, bool
                 : (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 
+// ---- LDS staging ----------------------------------------------------------------
+//
+// A per-lane piece of 16, 8 or 4 bytes is copied from a buffer straight into
+// LDS by the buffer-load-to-LDS instruction: one 16-byte transfer (lane l
+// lands at +16 l) or one 4-byte transfer per word (lane l at +4 l, one
+// 256-byte run per word).  A wave that reads the piece back from the same lane
+// positions gets what a direct load would have given it; past the buffer bound
+// the transfer writes zeros.  The LDS destination must be wave-uniform.
+//
+// The transfers are issued from inline assembly, so the compiler does not
+// count them when it places its own waits (which only makes those waits
+// stricter); the issuing wave waits for them with wait_vmcnt and a barrier
+// publishes them to the other waves.  The statements keep their place among
+// the kernel's memory accesses.  M0, which holds the LDS destination, is
+// restored afterwards.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ uint32_t lds_address(void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)p;
+}
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t off, void* dst) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(lds_address(dst)), "s"(r)
+      : "memory");
+}
+__device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t off, void* dst) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\t"
+      "buffer_load_dword %1, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(lds_address(dst)), "s"(r)
+      : "memory");
+}
+
+template <typename Raw>
+struct LdsPiece;
+template <>
+struct LdsPiece<uint4> {
+  static constexpr int kTransfers = 1;
+  static constexpr int kBytes = 64 * 16;
+  static __device__ __forceinline__ void copy(rsrc_t r, uint32_t off, char* dst) {
+    lds_load16(r, off, dst);
+  }
+  static __device__ __forceinline__ uint4 read(const char* src, int lane) {
+    return *reinterpret_cast<const uint4*>(src + 16 * lane);
+  }
+};
+template <>
+struct LdsPiece<uint2> {
+  static constexpr int kTransfers = 2;
+  static constexpr int kBytes = 64 * 8;
+  static __device__ __forceinline__ void copy(rsrc_t r, uint32_t off, char* dst) {
+    lds_load4(r, off, dst);
+    lds_load4(r, off + 4, dst + 256);
+  }
+  static __device__ __forceinline__ uint2 read(const char* src, int lane) {
+    return make_uint2(*reinterpret_cast<const uint32_t*>(src + 4 * lane),
+                      *reinterpret_cast<const uint32_t*>(src + 256 + 4 * lane));
+  }
+};
+template <>
+struct LdsPiece<uint32_t> {
+  static constexpr int kTransfers = 1;
+  static constexpr int kBytes = 64 * 4;
+  static __device__ __forceinline__ void copy(rsrc_t r, uint32_t off, char* dst) {
+    lds_load4(r, off, dst);
+  }
+  static __device__ __forceinline__ uint32_t read(const char* src, int lane) {
+    return *reinterpret_cast<const uint32_t*>(src + 4 * lane);
+  }
+};
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that the compiler may not move LDS accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---- FP8 E4M3 caches ----------------------------------------------------------
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -262,3 +262,28 @@ def test_fp8_workload_full_size():
     ref = oracle_ref(inp, seqs)
     for engine in ("auto", "valu"):
         compare(run(inp, engine=engine), ref, "bf16", seqs, what=f"fp8 gqa4096 b64 {engine}")
+
+
+# ---------------------------------------------------------------------------
+# Groups of more than 16 heads: the head-tile waves of a token group share
+# each K/V tile through an LDS ring and read block ids from an LDS window of
+# the table (512 entries), refilled as the walk moves on.  Long contexts at
+# small block sizes cross that window.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("group", [20, 48, 64])
+@pytest.mark.parametrize("kv", ["native", "fp8"])
+@pytest.mark.parametrize("head_size", [64, 128])
+def test_shared_tile_groups(group, kv, head_size):
+    dev = device()
+    dtype = "bf16" if head_size == 128 else "f16"
+    for block_size, lens in ((8, [1, 9, 300, 4500]), (16, [17, 1000, 8300]), (64, [63, 65, 2000])):
+        inp = to_device(make(num_seqs=len(lens), num_heads=group, num_kv_heads=1,
+                             head_size=head_size, block_size=block_size, dtype=dtype,
+                             seed=group + head_size + block_size, context_lens=lens, alibi=True,
+                             poison=True, kv_dtype="fp8" if kv == "fp8" else None,
+                             kv_scale=0.0625), dev)
+        ref = oracle_ref(inp)
+        for ps in (-1, 0, max(block_size, 128)):
+            compare(run(inp, engine="mfma", partition_size=ps), ref, dtype,
+                    what=f"G={group} {kv} D={head_size} BS={block_size} partition={ps}")
