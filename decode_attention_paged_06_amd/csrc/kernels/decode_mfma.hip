@@ -165,7 +165,35 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const int nrows = n_new * G;
   if (row_base >= nrows) return;  // this sequence has fewer rows
 
-  const int L = min(a.context_lens[seq], a.max_blocks_per_seq * BS);
+  // The query rows, and the block ids of this wave's first two tiles (their
+  // table positions do not depend on the context length), are requested
+  // before the context length is known, so the three loads overlap.
+  const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+  const int tile0 = part * a.partition_blocks * BS / TT;  // first tile of the partition
+  auto block_at = [&](int u) {  // table entry of tile u (clamped to the table)
+    return table[min((tile0 + u) >> tpb_shift, a.max_blocks_per_seq - 1)];
+  };
+  const int ctx_len = a.context_lens[seq];
+  int blk_first = 0, blk_second = 0;
+  if constexpr (!STAGE) {
+    blk_first = block_at(tg);
+    blk_second = block_at(tg + TG);
+  }
+  // ---- shared query load: the owned rows, zero-padded to NT * 16 ----------
+  __shared__ uint4 q_lds[NT * 16 * CH];
+  for (int idx = threadIdx.x; idx < NT * 16 * CH; idx += NTHREADS) {
+    const int rr = row_base + idx / CH;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (rr < nrows) {
+      const int ti = rr / G;
+      v = reinterpret_cast<const uint4*>(a.q)[((size_t)(q_first + ti) * a.num_heads + h0 + rr - ti * G) *
+                                                  CH + idx % CH];
+    }
+    q_lds[idx] = v;
+  }
+  asm volatile("" ::"s"(ctx_len));  // its load was in flight with the query's
+  __syncthreads();
+  const int L = min(ctx_len, a.max_blocks_per_seq * BS);
   if (L <= 0) {
     if (single) {  // no context: zero output rows
       for (int idx = threadIdx.x; idx < NT * 16 * CH; idx += NTHREADS) {
@@ -185,22 +213,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const int tok0 = part * a.partition_blocks * BS;
   if (tok0 >= kend) return;  // partition past every owned row's keys: nothing to do
   const int tok1 = min(kend, tok0 + a.partition_blocks * BS);
-  const int tile0 = tok0 / TT;                     // first tile of the partition
   const int ntiles = (tok1 - tok0 + TT - 1) / TT;  // tiles holding its tokens
 
-  // ---- shared query load: the owned rows, zero-padded to NT * 16 ----------
-  __shared__ uint4 q_lds[NT * 16 * CH];
-  for (int idx = threadIdx.x; idx < NT * 16 * CH; idx += NTHREADS) {
-    const int rr = row_base + idx / CH;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (rr < nrows) {
-      const int ti = rr / G;
-      v = reinterpret_cast<const uint4*>(a.q)[((size_t)(q_first + ti) * a.num_heads + h0 + rr - ti * G) *
-                                                  CH + idx % CH];
-    }
-    q_lds[idx] = v;
-  }
-  __syncthreads();
   const int row = row_base + tile * 16 + r;  // this lane's row
   const bool row_ok = row < nrows;
   const int ti = row / G;                    // its new token
@@ -224,7 +238,6 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 #pragma unroll
   for (int t = 0; t < EPL; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
   // Byte addressing: a wave-uniform tile base (SGPRs) plus a small unsigned
   // per-lane offset, so every K/V load is one buffer load with a VGPR offset.
   const size_t bstride = (size_t)a.num_kv_heads * BS * D * ES;  // bytes per physical block
@@ -246,7 +259,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   // anything, NaN included) read back as zeros, and a tile past the end of
   // the partition (u >= ntiles) reads nothing at all.  Every pipeline step
   // thus issues the same loads, which keeps the wait counts exact.
-  auto block_of = [&](int u) { return table[(tile0 + min(u, ntiles - 1)) >> tpb_shift]; };
+  auto block_of = [&](int u) { return block_at(min(u, ntiles - 1)); };
   auto load = [&](Tile& T, int u, int blk) {
     const int ua = tile0 + u;
     const size_t off = (size_t)blk * bstride + (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
@@ -326,9 +339,9 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     Tile buf[kDepth];
     int u = tg;
     if (u < ntiles) {
-#pragma unroll
-      for (int k = 0; k + 1 < kDepth; ++k) load(buf[k], u + k * TG, block_of(u + k * TG));
-      int blk_next = block_of(u + (kDepth - 1) * TG);
+      static_assert(kDepth == 2, "the prologue uses the two prefetched block ids");
+      load(buf[0], u, blk_first);
+      int blk_next = u + TG < ntiles ? blk_second : blk_first;
       bool more = true;
       while (more) {
 #pragma unroll

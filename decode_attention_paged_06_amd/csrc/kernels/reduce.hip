@@ -11,17 +11,84 @@
 //   M = max_p m_p,  w_p = l_p * exp2(m_p - M),  out = sum_p w_p o_p / sum_p w_p
 // over the partitions that hold keys the row sees (p < ceil(visible /
 // partition_size), visible = L_s for decode, position + 1 for a new token of a
-// multi-query call).  One wave per (head, sequence, new token); lane k owns
-// D/64 output elements.
+// multi-query call).  One wave per (head, sequence, new token).  The (m_p,
+// l_p) pairs are read one partition per lane (64 at a time) and reduced across
+// the wave; the partial outputs are read in batches whose loads are all in
+// flight together, so a row costs a few memory round trips however many
+// partitions it has.
+#include <type_traits>
+
 #include "../launch.h"
 #include "device_common.h"
 
 namespace pa {
 
+// Maximum / sum over the 64 lanes of a wave; every lane receives the result.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return column_max4(x);
+}
+__device__ __forceinline__ float wave_sum(float x) { return column_sum4(group_sum<16>(x)); }
+
+// Weighted sum of a row's active partitions.  Lane k holds D/64 elements of
+// every partial output; NB partial-output loads per lane are in flight at a
+// time (NB chosen from the partition count so that no load is wasted on a
+// short row).  The first batch is requested before the weights are known, so
+// its loads overlap the (m, l) round trip.
+template <int NB, typename Part>
+__device__ __forceinline__ void weighted_sum(const float2* ml, const Part* o, int nact, int stride,
+                                             int lane, float& wsum, float& acc0, float& acc1) {
+  Part v[NB];
+  auto fetch = [&](int first) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) v[k] = o[(size_t)min(first + k, nact - 1) * stride];
+  };
+  // lane k holds (m, l) of partition k of the first 64; M = max_p m_p
+  const float2 s0 = ml[min(lane, nact - 1)];
+  fetch(0);
+  const float m0 = lane < nact ? s0.x : kNegBig;
+  const float l0 = lane < nact ? s0.y : 0.f;
+  float M = m0;
+  for (int c = 64; c < nact; c += 64) M = fmaxf(M, c + lane < nact ? ml[c + lane].x : kNegBig);
+  M = wave_max(M);
+
+  for (int c = 0; c < nact; c += 64) {
+    // lane k holds the weight of partition c + k (0 past the last one)
+    float w = 0.f;
+    if (c == 0) {
+      w = lane < nact ? l0 * fast_exp2(m0 - M) : 0.f;
+    } else if (c + lane < nact) {
+      const float2 s = ml[c + lane];
+      w = s.y * fast_exp2(s.x - M);
+    }
+    wsum += w;
+    const int n = min(64, nact - c);
+    for (int b = 0; b < n; b += NB) {
+      // every load is issued (indices past the last partition re-read it and
+      // get weight 0), so all NB loads are in flight together
+      if (c + b > 0) fetch(c + b);
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), b + k));
+        if constexpr (sizeof(Part) == 8) {
+          acc0 = fmaf(wk, v[k].x, acc0);
+          acc1 = fmaf(wk, v[k].y, acc1);
+        } else {
+          acc0 = fmaf(wk, v[k], acc0);
+        }
+      }
+    }
+  }
+}
+
 template <typename Fmt, int D>
 __global__ __launch_bounds__(64) void partition_reduce_kernel(const DecodeArgs a) {
   constexpr int PER = D / 64;
   static_assert(PER == 1 || PER == 2, "head size 64 or 128");
+  using Part = typename std::conditional<PER == 2, float2, float>::type;
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int i = blockIdx.z;  // new token of the sequence (0 for decode)
@@ -46,23 +113,13 @@ __global__ __launch_bounds__(64) void partition_reduce_kernel(const DecodeArgs a
   const int visible = L - n_new + i + 1;
   const int nact = min(a.num_partitions, (visible + ptok - 1) / ptok);
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + row * a.num_partitions;
-  const float* o = a.ws_o + row * a.num_partitions * D + lane * PER;
+  const Part* o = reinterpret_cast<const Part*>(a.ws_o + row * a.num_partitions * D) + lane;
 
-  float M = kNegBig;
-  for (int p = 0; p < nact; ++p) M = fmaxf(M, ml[p].x);
   float wsum = 0.f, acc0 = 0.f, acc1 = 0.f;
-  for (int p = 0; p < nact; ++p) {
-    const float2 s = ml[p];
-    const float w = s.y * fast_exp2(s.x - M);
-    wsum += w;
-    if constexpr (PER == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(o + (size_t)p * D);
-      acc0 = fmaf(w, v.x, acc0);
-      acc1 = fmaf(w, v.y, acc1);
-    } else {
-      acc0 = fmaf(w, o[(size_t)p * D], acc0);
-    }
-  }
+  if (nact <= 4) weighted_sum<4>(ml, o, nact, D / PER, lane, wsum, acc0, acc1);
+  else if (nact <= 8) weighted_sum<8>(ml, o, nact, D / PER, lane, wsum, acc0, acc1);
+  else weighted_sum<16>(ml, o, nact, D / PER, lane, wsum, acc0, acc1);
+  wsum = wave_sum(wsum);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   if constexpr (PER == 2) {
     *reinterpret_cast<uint32_t*>(orow) = Fmt::pack(acc0 * inv, acc1 * inv);
