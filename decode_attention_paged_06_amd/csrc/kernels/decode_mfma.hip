@@ -339,9 +339,12 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     Tile buf[kDepth];
     int u = tg;
     if (u < ntiles) {
-      static_assert(kDepth == 2, "the prologue uses the two prefetched block ids");
+      // the first two block ids were fetched with the query
+      const int blk_1 = u + TG < ntiles ? blk_second : blk_first;
       load(buf[0], u, blk_first);
-      int blk_next = u + TG < ntiles ? blk_second : blk_first;
+#pragma unroll
+      for (int k = 1; k + 1 < kDepth; ++k) load(buf[k], u + k * TG, k == 1 ? blk_1 : block_of(u + k * TG));
+      int blk_next = kDepth == 2 ? blk_1 : block_of(u + (kDepth - 1) * TG);
       bool more = true;
       while (more) {
 #pragma unroll
