@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "longest_first"],
+                    help="order of the work units of a split plan (see pa_schedule)")
     ap.add_argument("--kv-dtype", default=None, choices=["fp8"],
                     help="store the K/V caches as FP8 E4M3 (scale 1/16) instead of the query type")
     ap.add_argument("--block-size", type=int, default=0,
@@ -320,7 +322,7 @@ def main():
 
     dims = make_dims(first.query, first.key_cache, first.block_tables, first.k_scale,
                      first.v_scale)
-    opts = make_opts(a.partition_size, a.engine)
+    opts = make_opts(a.partition_size, a.engine, schedule=a.schedule)
     plan = paged_attention_plan(dims, 1 << 40, opts)
     workspace = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
                  if plan.workspace_bytes else None)
@@ -331,7 +333,7 @@ def main():
                                s.block_tables, s.context_lens, s.scale, s.block_size,
                                s.alibi_slopes, workspace=workspace,
                                partition_size=a.partition_size, engine=a.engine,
-                               k_scale=s.k_scale, v_scale=s.v_scale)
+                               k_scale=s.k_scale, v_scale=s.v_scale, schedule=a.schedule)
 
     for i in range(a.warmup):
         step(i)
@@ -414,6 +416,7 @@ def main():
             "context_lens": str(args["context_lens"]), "seed": args["seed"],
             "engine": {0: "auto", 1: "valu", 2: "mfma"}[plan.engine] if a.engine == "auto" else a.engine,
             "num_partitions": plan.num_partitions, "partition_size": plan.partition_size,
+            "schedule": {1: "grid", 2: "longest_first"}[plan.schedule],
             "input_sets_rotated": nsets,
         },
         "us_per_call": round(ms_per_step * 1e3, 2),

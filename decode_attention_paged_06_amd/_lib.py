@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libpagedattn.so")
 PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_KV_NATIVE, PA_KV_FP8_E4M3 = 0, 1
 PA_ENGINE_AUTO, PA_ENGINE_VALU, PA_ENGINE_MFMA = 0, 1, 2
+PA_SCHEDULE_AUTO, PA_SCHEDULE_GRID, PA_SCHEDULE_LONGEST_FIRST = 0, 1, 2
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_ALIGNMENT",
           4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH", 6: "PA_ERR_DEVICE"}
 
@@ -35,12 +36,12 @@ class PaDims(ctypes.Structure):
 
 class PaOpts(ctypes.Structure):
     _fields_ = [("partition_size", ctypes.c_int32), ("engine", ctypes.c_int32),
-                ("num_cus", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("num_cus", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
 class PaPlan(ctypes.Structure):
     _fields_ = [("num_partitions", ctypes.c_int32), ("partition_size", ctypes.c_int32),
-                ("engine", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("engine", ctypes.c_int32), ("schedule", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 

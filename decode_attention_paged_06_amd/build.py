@@ -26,6 +26,7 @@ SOURCES = [
     "kernels/decode_mfma.hip",
     "kernels/reduce.hip",
     "kernels/gather.hip",
+    "kernels/schedule.hip",
 ]
 
 ARCH = "gfx950"

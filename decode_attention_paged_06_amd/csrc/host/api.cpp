@@ -111,11 +111,23 @@ CallShape decode_shape(const pa_dims* d) {
   return c;
 }
 
-// Workspace bytes for P partitions: fp32 partial outputs, then (m, l) pairs.
-size_t split_workspace(const pa_dims* d, const CallShape& c, int P) {
-  if (P <= 1) return 0;
+// Workspace of a split plan: fp32 partial outputs, then (m, l) pairs, then
+// (longest-first schedule only) the order of the num_seqs * P work units.
+struct SplitLayout {
+  size_t ml_offset = 0, order_offset = 0, bytes = 0;
+};
+SplitLayout split_layout(const pa_dims* d, const CallShape& c, int P, bool longest_first) {
+  SplitLayout w;
+  if (P <= 1) return w;
   const size_t rows = (size_t)c.rows * d->num_heads * P;
-  return align_up(rows * d->head_size * sizeof(float), kWsAlign) + rows * 2 * sizeof(float);
+  w.ml_offset = align_up(rows * d->head_size * sizeof(float), kWsAlign);
+  w.order_offset = align_up(w.ml_offset + rows * 2 * sizeof(float), kWsAlign);
+  w.bytes = longest_first ? w.order_offset + (size_t)d->num_seqs * P * sizeof(int32_t)
+                          : w.ml_offset + rows * 2 * sizeof(float);
+  return w;
+}
+size_t split_workspace(const pa_dims* d, const CallShape& c, int P, bool longest_first) {
+  return split_layout(d, c, P, longest_first).bytes;
 }
 
 int resolve_engine(const pa_dims* d, const CallShape& c, const pa_opts* o, int* engine) {
@@ -156,6 +168,18 @@ int make_plan(const pa_dims* d, const CallShape& c, size_t ws_bytes, const pa_op
   if ((st = resolve_engine(d, c, o, &engine))) return st;
   const int maxb = d->max_blocks_per_seq;
   const int forced = o ? o->partition_size : 0;
+  const int group = d->num_heads / d->num_kv_heads;
+  const int schedule = o ? o->schedule : PA_SCHEDULE_AUTO;
+  if (schedule != PA_SCHEDULE_AUTO && schedule != PA_SCHEDULE_GRID &&
+      schedule != PA_SCHEDULE_LONGEST_FIRST)
+    return fail(PA_ERR_INVALID_ARG, "schedule %d", schedule);
+  // Longest-first ordering applies to split decode plans on the MFMA engine;
+  // automatic for groups of more than 16 heads (48-head MQA with ragged
+  // lengths measured faster), on request otherwise.
+  const bool longest_first =
+      engine == PA_ENGINE_MFMA && !c.multi &&
+      (schedule == PA_SCHEDULE_LONGEST_FIRST ||
+       (schedule == PA_SCHEDULE_AUTO && pa::mfma_head_tiles(group) > 1));
   int P = 1, PB = maxb;
 
   if (forced == -1) {
@@ -167,14 +191,13 @@ int make_plan(const pa_dims* d, const CallShape& c, size_t ws_bytes, const pa_op
     PB = forced / d->block_size;
     P = (maxb + PB - 1) / PB;
     if (P > 65535) return fail(PA_ERR_INVALID_ARG, "partition_size %d gives %d partitions", forced, P);
-    if (P > 1 && !unlimited && split_workspace(d, c, P) > ws_bytes)
+    if (P > 1 && !unlimited && split_workspace(d, c, P, longest_first) > ws_bytes)
       return fail(PA_ERR_WORKSPACE, "forced partition_size %d needs %zu workspace bytes, got %zu",
-                  forced, split_workspace(d, c, P), ws_bytes);
+                  forced, split_workspace(d, c, P, longest_first), ws_bytes);
   } else if (forced == 0) {
     int cus = o ? o->num_cus : 0;
     if (cus < 0) return fail(PA_ERR_INVALID_ARG, "num_cus = %d", cus);
     if (cus == 0 && (st = current_num_cus(&cus))) return st;
-    const int group = d->num_heads / d->num_kv_heads;
     const long long units = (long long)d->num_seqs * d->num_kv_heads * row_chunks(d, c, engine);
     const bool multi_tile =
         engine == PA_ENGINE_MFMA && !c.multi && pa::mfma_head_tiles(group) > 1;
@@ -187,7 +210,7 @@ int make_plan(const pa_dims* d, const CallShape& c, size_t ws_bytes, const pa_op
       if (PB < min_pb) PB = min_pb;
       P = (maxb + PB - 1) / PB;
       // shrink to what the workspace holds
-      while (P > 1 && !unlimited && split_workspace(d, c, P) > ws_bytes) {
+      while (P > 1 && !unlimited && split_workspace(d, c, P, longest_first) > ws_bytes) {
         PB *= 2;
         P = (maxb + PB - 1) / PB;
       }
@@ -203,8 +226,8 @@ int make_plan(const pa_dims* d, const CallShape& c, size_t ws_bytes, const pa_op
   p->num_partitions = P;
   p->partition_size = PB * d->block_size;
   p->engine = engine;
-  p->reserved = 0;
-  p->workspace_bytes = split_workspace(d, c, P);
+  p->schedule = P > 1 && longest_first ? PA_SCHEDULE_LONGEST_FIRST : PA_SCHEDULE_GRID;
+  p->workspace_bytes = split_workspace(d, c, P, longest_first);
   return PA_OK;
 }
 
@@ -273,16 +296,26 @@ int run_attention(void* out, const void* query, const void* key_cache, const voi
   a.row_chunks = (int32_t)(plan.engine == PA_ENGINE_MFMA ? row_chunks(dims, c, plan.engine) : 1);
   a.ws_o = nullptr;
   a.ws_ml = nullptr;
+  a.unit_order = nullptr;
+  const bool longest_first = plan.schedule == PA_SCHEDULE_LONGEST_FIRST;
+  int32_t* order = nullptr;
   if (plan.num_partitions > 1) {
-    const size_t rows = (size_t)c.rows * dims->num_heads * plan.num_partitions;
+    const SplitLayout w = split_layout(dims, c, plan.num_partitions, longest_first);
     a.ws_o = static_cast<float*>(workspace);
-    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       align_up(rows * dims->head_size * sizeof(float), kWsAlign));
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.ml_offset);
+    if (longest_first) order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + w.order_offset);
   }
   if ((long long)dims->num_kv_heads * a.row_chunks > 0x7fffffffLL)
     return fail(PA_ERR_INVALID_ARG, "too many query rows per sequence");
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (order != nullptr) {
+    if ((long long)dims->num_kv_heads * a.row_chunks * dims->num_seqs * plan.num_partitions > 0x7fffffffLL)
+      return fail(PA_ERR_INVALID_ARG, "too many work units for a longest-first schedule");
+    hipError_t e = pa::launch_unit_order(a, order, s);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "schedule launch: %s", hipGetErrorString(e));
+    a.unit_order = order;
+  }
   hipError_t e = plan.engine == PA_ENGINE_MFMA
                      ? pa::launch_decode_mfma(a, dims->dtype, dims->head_size, kv_fp8, s)
                      : pa::launch_decode_valu(a, dims->dtype, dims->head_size, kv_fp8, s);

@@ -149,10 +149,17 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   // numbered i * G + g; the workgroup owns NT * 16 consecutive rows.  Decode
   // has one new token per sequence, so its rows are the group's G heads.
   const int chunks = a.row_chunks;
-  const int kvh = blockIdx.x / chunks;
-  const int rc = blockIdx.x - kvh * chunks;
-  const int seq = blockIdx.y;
-  const int part = blockIdx.z;
+  int xi = blockIdx.x, seq = blockIdx.y, part = blockIdx.z;
+  if (a.unit_order != nullptr) {  // longest-first schedule over a 1-D grid
+    const int X = a.num_kv_heads * chunks;
+    const int n = blockIdx.x / X;
+    const int unit = a.unit_order[n];
+    xi = blockIdx.x - n * X;
+    seq = unit % a.num_seqs;
+    part = unit / a.num_seqs;
+  }
+  const int kvh = xi / chunks;
+  const int rc = xi - kvh * chunks;
   const int G = a.group;
   const int h0 = kvh * G;
   const bool single = a.num_partitions == 1;
@@ -498,7 +505,9 @@ namespace {
 
 template <typename Fmt, int D, int NT, int TG, bool KV8>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.num_kv_heads * a.row_chunks, a.num_seqs, a.num_partitions);
+  const dim3 grid = a.unit_order != nullptr
+                       ? dim3(a.num_kv_heads * a.row_chunks * a.num_seqs * a.num_partitions)
+                       : dim3(a.num_kv_heads * a.row_chunks, a.num_seqs, a.num_partitions);
   decode_mfma_kernel<Fmt, D, NT, TG, KV8><<<grid, NT * TG * 64, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -44,6 +44,10 @@ struct DecodeArgs {
   const int32_t* query_start;
   int32_t max_new_tokens;       // bound on new tokens per sequence (1 for decode)
   int32_t row_chunks;           // workgroups per (sequence, kv head) over the query rows
+  // Longest-first schedule: the decode grid is 1-D, workgroup b takes
+  // (sequence, partition) unit_order[b / (num_kv_heads * row_chunks)], encoded
+  // partition * num_seqs + sequence.  nullptr = the grid's own order.
+  const int32_t* unit_order = nullptr;
 };
 
 // Head tiles of the MFMA decode workgroup for a group size, and the query-row
@@ -66,6 +70,12 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, boo
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, bool kv_fp8,
                               hipStream_t s);
 hipError_t launch_partition_reduce(const DecodeArgs& a, int dtype, int head_size, hipStream_t s);
+
+// Writes the num_seqs * num_partitions decode units (sequence, partition),
+// encoded partition * num_seqs + sequence, to `order` sorted by decreasing
+// token count (in buckets of partition_size / 62 tokens; order within a
+// bucket unspecified), empty units last.
+hipError_t launch_unit_order(const DecodeArgs& a, int32_t* order, hipStream_t s);
 
 // Row copies move row_bytes-long rows (a multiple of 16) between the cache and
 // contiguous [num_tokens, num_kv_heads] row arrays.

@@ -12,10 +12,13 @@ import torch
 
 from . import _lib
 from ._lib import (PA_BF16, PA_ENGINE_AUTO, PA_ENGINE_MFMA, PA_ENGINE_VALU, PA_F16, PA_FP8_E4M3,
-                   PA_KV_FP8_E4M3, PA_KV_NATIVE, PaDims, PaOpts, PaPlan, check, lib)
+                   PA_KV_FP8_E4M3, PA_KV_NATIVE, PA_SCHEDULE_AUTO, PA_SCHEDULE_GRID,
+                   PA_SCHEDULE_LONGEST_FIRST, PaDims, PaOpts, PaPlan, check, lib)
 
 _DTYPE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_FP8_E4M3}
 _ENGINE = {"auto": PA_ENGINE_AUTO, "valu": PA_ENGINE_VALU, "mfma": PA_ENGINE_MFMA}
+_SCHEDULE = {"auto": PA_SCHEDULE_AUTO, "grid": PA_SCHEDULE_GRID,
+             "longest_first": PA_SCHEDULE_LONGEST_FIRST}
 
 
 def make_dims(query: torch.Tensor, key_cache: torch.Tensor, block_tables: torch.Tensor,
@@ -27,8 +30,9 @@ def make_dims(query: torch.Tensor, key_cache: torch.Tensor, block_tables: torch.
                   PA_KV_FP8_E4M3 if fp8 else PA_KV_NATIVE, float(k_scale), float(v_scale))
 
 
-def make_opts(partition_size: int = 0, engine: str = "auto", num_cus: int = 0) -> PaOpts:
-    return PaOpts(int(partition_size), _ENGINE[engine], int(num_cus), 0)
+def make_opts(partition_size: int = 0, engine: str = "auto", num_cus: int = 0,
+              schedule: str = "auto") -> PaOpts:
+    return PaOpts(int(partition_size), _ENGINE[engine], int(num_cus), _SCHEDULE[schedule])
 
 
 def _stream_ptr(stream) -> Optional[int]:
@@ -64,7 +68,7 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
                            alibi_slopes: Optional[torch.Tensor] = None, stream=None,
                            workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
                            engine: str = "auto", k_scale: float = 1.0,
-                           v_scale: float = 1.0) -> torch.Tensor:
+                           v_scale: float = 1.0, schedule: str = "auto") -> torch.Tensor:
     """Enqueue paged decode attention; writes and returns ``out`` ([S, Hq, D]).
 
     Caches hold the query's dtype, or torch.float8_e4m3fn with the real values
@@ -83,7 +87,7 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
     if query.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {query.dtype}")
     dims = make_dims(query, key_cache, block_tables, k_scale, v_scale)
-    opts = make_opts(partition_size, engine)
+    opts = make_opts(partition_size, engine, schedule=schedule)
     if workspace is None:
         nbytes = paged_attention_workspace_bytes(dims, opts)
         if nbytes:

@@ -107,14 +107,25 @@ typedef enum {
   PA_ENGINE_MFMA = 2  /* matrix cores: the query group as a 16-wide MFMA tile           */
 } pa_engine;
 
+/* Order in which the work units (sequence, partition) of a split decode plan
+ * on the matrix-core engine are started.  With ragged context lengths the
+ * units differ in size; starting the longest first (a small ordering kernel
+ * runs before the decode kernel) shortens the tail of the launch.  Results
+ * are identical either way. */
+typedef enum {
+  PA_SCHEDULE_AUTO = 0,          /* longest first for groups of more than 16 heads */
+  PA_SCHEDULE_GRID = 1,          /* the grid's order (partition-major)              */
+  PA_SCHEDULE_LONGEST_FIRST = 2  /* longest first whenever the plan splits (MFMA)   */
+} pa_schedule;
+
 /* Optional overrides (pass NULL for the defaults). */
 typedef struct {
   /* 0: the planner decides; -1: force one pass per (sequence, kv head);
    * > 0: force partitions of this many tokens (a multiple of block_size). */
   int32_t partition_size;
-  int32_t engine;  /* pa_engine */
-  int32_t num_cus; /* 0: query the current device; > 0: plan for this many CUs */
-  int32_t reserved;
+  int32_t engine;   /* pa_engine */
+  int32_t num_cus;  /* 0: query the current device; > 0: plan for this many CUs */
+  int32_t schedule; /* pa_schedule */
 } pa_opts;
 
 /* A launch plan (output of paged_attention_plan). */
@@ -122,7 +133,7 @@ typedef struct {
   int32_t num_partitions; /* partitions per sequence; 1 = single pass, no reduce  */
   int32_t partition_size; /* tokens per partition (multiple of block_size)         */
   int32_t engine;         /* resolved pa_engine                                     */
-  int32_t reserved;
+  int32_t schedule;       /* resolved: PA_SCHEDULE_GRID or PA_SCHEDULE_LONGEST_FIRST */
   size_t workspace_bytes; /* workspace this plan uses (0 for a single pass)         */
 } pa_plan;
 

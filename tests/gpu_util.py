@@ -29,13 +29,13 @@ def to_device(inp, dev):
     return inp
 
 
-def run(inp, engine="auto", partition_size=0, out=None):
+def run(inp, engine="auto", partition_size=0, out=None, schedule="auto"):
     if out is None:
         out = torch.full_like(inp.query, float("nan"))
     paged_attention_decode(out, inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
                            inp.context_lens, inp.scale, inp.block_size, inp.alibi_slopes,
                            partition_size=partition_size, engine=engine,
-                           k_scale=inp.k_scale, v_scale=inp.v_scale)
+                           k_scale=inp.k_scale, v_scale=inp.v_scale, schedule=schedule)
     torch.cuda.synchronize()
     return out
 

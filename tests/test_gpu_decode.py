@@ -287,3 +287,23 @@ def test_shared_tile_groups(group, kv, head_size):
         for ps in (-1, 0, max(block_size, 128)):
             compare(run(inp, engine="mfma", partition_size=ps), ref, dtype,
                     what=f"G={group} {kv} D={head_size} BS={block_size} partition={ps}")
+
+
+# ---------------------------------------------------------------------------
+# Longest-first schedule of split units: only the order in which workgroups
+# start changes, so the results are bit-identical to the grid order.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("group,Hkv", [(48, 1), (8, 2)])
+def test_longest_first_schedule(group, Hkv):
+    dev = device()
+    inp = to_device(make(num_seqs=40, num_heads=group * Hkv, num_kv_heads=Hkv, head_size=128,
+                         block_size=16, dtype="f16", seed=4040 + group, context_lens=(1, 3000),
+                         alibi=True, poison=True), dev)
+    seqs = sample_seqs(40, 12, seed=group)
+    ref = oracle_ref(inp, seqs)
+    for ps in (0, 128, 512):
+        grid = run(inp, engine="mfma", partition_size=ps, schedule="grid")
+        lpt = run(inp, engine="mfma", partition_size=ps, schedule="longest_first")
+        assert torch.equal(grid, lpt), f"G={group} partition={ps}: schedules differ"
+        compare(lpt, ref, "f16", seqs, what=f"longest-first G={group} partition={ps}")

@@ -65,9 +65,9 @@ def dims(S=256, Hq=64, Hkv=8, D=128, BS=16, NB=65536, MAXB=256, dtype=1):
     return PaDims(S, Hq, Hkv, D, BS, NB, MAXB, dtype)
 
 
-def plan(L, d, ws=1 << 40, ps=0, engine=0, cus=256):
+def plan(L, d, ws=1 << 40, ps=0, engine=0, cus=256, schedule=0):
     p = PaPlan()
-    st = L.paged_attention_plan(ctypes.byref(d), ws, ctypes.byref(PaOpts(ps, engine, cus, 0)),
+    st = L.paged_attention_plan(ctypes.byref(d), ws, ctypes.byref(PaOpts(ps, engine, cus, schedule)),
                                 ctypes.byref(p))
     return st, p
 
@@ -258,6 +258,31 @@ def test_plan_multi_tile_partitions(L):
     # 48-head MQA, batch 256, contexts up to 8192: four partitions per sequence
     st, p = plan(L, dims(S=256, Hq=48, Hkv=1, MAXB=512))
     assert st == OK and p.engine == 2 and p.num_partitions == 4
+
+
+def test_plan_schedule(L):
+    GRID, LONGEST = 1, 2
+    mqa = dims(S=256, Hq=48, Hkv=1, MAXB=512)
+    st, p = plan(L, mqa)                                   # split, > 16 heads: longest first
+    assert st == OK and p.num_partitions > 1 and p.schedule == LONGEST
+    st, g = plan(L, mqa, schedule=GRID)
+    assert st == OK and g.schedule == GRID and g.num_partitions == p.num_partitions
+    # the unit order (one int32 per (sequence, partition)) sits after the partials
+    assert p.workspace_bytes >= g.workspace_bytes + 256 * p.num_partitions * 4
+    st, p = plan(L, dims(S=4))                             # split GQA: grid order unless asked
+    assert st == OK and p.num_partitions > 1 and p.schedule == GRID
+    st, p = plan(L, dims(S=4), schedule=LONGEST)
+    assert st == OK and p.schedule == LONGEST
+    st, p = plan(L, dims(S=256), schedule=LONGEST)         # single pass: nothing to order
+    assert st == OK and p.num_partitions == 1 and p.schedule == GRID and p.workspace_bytes == 0
+    st, p = plan(L, dims(S=4, Hq=8, Hkv=8), schedule=LONGEST)  # VALU engine keeps the grid
+    assert st == OK and p.engine == 1 and p.schedule == GRID
+    assert plan(L, dims(), schedule=3)[0] == INVALID
+    assert plan(L, dims(), schedule=-1)[0] == INVALID
+    d = dims(S=256, Hq=48, Hkv=1, MAXB=512)
+    o = PaOpts(0, 0, 256, 0)
+    assert L.paged_attention_workspace_bytes(ctypes.byref(d), ctypes.byref(o)) == \
+        plan(L, d)[1].workspace_bytes
 
 
 def test_status_strings(L):
