@@ -39,10 +39,11 @@
 // which is what lines these layouts up with coalesced loads and no LDS
 // staging of K or V.
 //
-// Softmax: fp32 online softmax in log2 units; the running max of a head is
-// shared by the 4 lane groups j (two lane swaps per tile), each lane keeps a
-// partial sum of its own rounded p values, and the accumulator rescale is
-// skipped when no lane's max moved.  P is rounded to the storage type before
+// Softmax: fp32 online softmax in log2 units against a reference max per
+// head, shared by the 4 lane groups j (two lane swaps per tile); each lane
+// keeps a partial sum of its own rounded p values.  The reference moves (and
+// l and the accumulators are rescaled) only when a tile's max exceeds it by
+// more than 8, so p stays below 2^8 and the rescale is rare.  P is rounded to the storage type before
 // the P.V product (the matrix cores take 16-bit operands); the sum l uses the
 // same rounded values so the normalisation matches what was accumulated.
 //
@@ -119,6 +120,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   using KRaw = typename KS::Raw8;                // 8 cached K elements as loaded
   using VRaw = typename std::conditional<EPL == 8, typename KS::Raw8, typename KS::Raw4>::type;
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay below 256
   constexpr int kDepth = 2;  // register tiles in the load pipeline (one wave per tile)
   // With several head tiles the NT waves of a token group need the same K/V
   // tile: it is staged once through a ring of kRing LDS slots instead.
@@ -315,18 +317,23 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
         x[v] = (t < valid && tb + t <= pos) ? z : kNegBig;
       }
     }
+    // The reference max m moves only when some row's tile max exceeds it by
+    // more than kRescaleSlack (weights then stay below 2^kRescaleSlack): the
+    // rescale of l and the accumulators is rare, and the result is the same
+    // quotient acc / l whichever m it is taken against.
     const float mx = column_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-    const float mn = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
-    const uint32_t p01 = Fmt::pack(fast_exp2(x[0] - mn), fast_exp2(x[1] - mn));
-    const uint32_t p23 = Fmt::pack(fast_exp2(x[2] - mn), fast_exp2(x[3] - mn));
-    const uint2 pk = make_uint2(p01, p23);
-    lsum = fmaf(lsum, alpha, (Fmt::lo(p01) + Fmt::hi(p01)) + (Fmt::lo(p23) + Fmt::hi(p23)));
-    if (wave_any(alpha != 1.f)) {
+    if (wave_any(mx > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      lsum *= alpha;
 #pragma unroll
       for (int t = 0; t < EPL; ++t) acc[t] *= alpha;
     }
+    const uint32_t p01 = Fmt::pack(fast_exp2(x[0] - m), fast_exp2(x[1] - m));
+    const uint32_t p23 = Fmt::pack(fast_exp2(x[2] - m), fast_exp2(x[3] - m));
+    const uint2 pk = make_uint2(p01, p23);
+    lsum += (Fmt::lo(p01) + Fmt::hi(p01)) + (Fmt::lo(p23) + Fmt::hi(p23));
 
 #pragma unroll
     for (int t = 0; t < EPL; ++t) {
