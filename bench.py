@@ -416,7 +416,7 @@ def main():
             "context_lens": str(args["context_lens"]), "seed": args["seed"],
             "engine": {0: "auto", 1: "valu", 2: "mfma"}[plan.engine] if a.engine == "auto" else a.engine,
             "num_partitions": plan.num_partitions, "partition_size": plan.partition_size,
-            "schedule": {1: "grid", 2: "longest_first"}[plan.schedule],
+            "schedule": {2: "longest_first"}.get(plan.schedule, "grid"),
             "input_sets_rotated": nsets,
         },
         "us_per_call": round(ms_per_step * 1e3, 2),

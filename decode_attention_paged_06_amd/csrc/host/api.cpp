@@ -33,9 +33,12 @@ constexpr size_t kWsAlign = 256;
 constexpr int kMaxDevices = 64;
 // Workgroups per CU the auto plan aims for before it splits contexts; groups
 // of more than 16 heads (several MFMA head tiles sharing every K/V block) are
-// split finer, which measured best for 48-head MQA with ragged lengths.
+// split finer, which measured best for 48-head MQA with ragged lengths, and
+// the VALU engine less (its split costs more than the grid fill gains on the
+// 40-head MHA batch: 320 workgroups run best as one pass).
 constexpr int kTargetGroupsPerCu = 2;
 constexpr int kTargetGroupsPerCuMultiTile = 4;
+constexpr int kTargetGroupsPerCuValu = 1;
 // Smallest partition the auto plan makes: 128 tokens (two 16-row tiles per wave).
 constexpr int kMinPartitionTokens = 128;
 
@@ -202,7 +205,9 @@ int make_plan(const pa_dims* d, const CallShape& c, size_t ws_bytes, const pa_op
     const bool multi_tile =
         engine == PA_ENGINE_MFMA && !c.multi && pa::mfma_head_tiles(group) > 1;
     const long long target =
-        (long long)(multi_tile ? kTargetGroupsPerCuMultiTile : kTargetGroupsPerCu) * cus;
+        (long long)(multi_tile ? kTargetGroupsPerCuMultiTile
+                               : engine == PA_ENGINE_VALU ? kTargetGroupsPerCuValu : kTargetGroupsPerCu) *
+        cus;
     const int min_pb = kMinPartitionTokens / d->block_size > 1 ? kMinPartitionTokens / d->block_size : 1;
     if (units > 0 && units < target && maxb > min_pb) {
       long long want = (target + units - 1) / units;
