@@ -307,3 +307,22 @@ def test_longest_first_schedule(group, Hkv):
         lpt = run(inp, engine="mfma", partition_size=ps, schedule="longest_first")
         assert torch.equal(grid, lpt), f"G={group} partition={ps}: schedules differ"
         compare(lpt, ref, "f16", seqs, what=f"longest-first G={group} partition={ps}")
+
+
+# ---------------------------------------------------------------------------
+# The reduce at every partition count it handles differently: batches of 4,
+# 8 and 16 partial-output loads, and more than 64 partitions (the (m, l)
+# pairs then take several passes of one partition per lane).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_reduce_partition_counts(engine):
+    dev = device()
+    lens = [1, 40, 100, 130, 250, 520, 1100, 2200]
+    inp = to_device(make(num_seqs=len(lens), num_heads=16, num_kv_heads=2, head_size=128,
+                         block_size=16, dtype="bf16", seed=64, context_lens=lens, alibi=True,
+                         poison=True), dev)
+    ref = oracle_ref(inp)
+    for ps in (16, 32, 64, 128, 256, 1024):  # up to 138 partitions of the longest sequence
+        compare(run(inp, engine=engine, partition_size=ps), ref, "bf16",
+                what=f"{engine} partition={ps}")
