@@ -31,13 +31,12 @@ int ok() {
 
 constexpr size_t kWsAlign = 256;
 constexpr int kMaxDevices = 64;
-// Workgroups per CU the auto plan aims for before it splits contexts; groups
-// of more than 16 heads (several MFMA head tiles sharing every K/V block) are
-// split finer, which measured best for 48-head MQA with ragged lengths, and
-// the VALU engine less (its split costs more than the grid fill gains on the
-// 40-head MHA batch: 320 workgroups run best as one pass).
+// Workgroups per CU the auto plan aims for before it splits contexts; the
+// VALU engine less (its split costs more than the grid fill gains on the
+// 40-head MHA batch: 320 workgroups run best as one pass).  For 48-head MQA
+// with ragged lengths (12-wave workgroups) two partitions of 4096 tokens
+// measured best (121 us against 134 with four).
 constexpr int kTargetGroupsPerCu = 2;
-constexpr int kTargetGroupsPerCuMultiTile = 4;
 constexpr int kTargetGroupsPerCuValu = 1;
 // Smallest partition the auto plan makes: 128 tokens (two 16-row tiles per wave).
 constexpr int kMinPartitionTokens = 128;
@@ -202,12 +201,8 @@ int make_plan(const pa_dims* d, const CallShape& c, size_t ws_bytes, const pa_op
     if (cus < 0) return fail(PA_ERR_INVALID_ARG, "num_cus = %d", cus);
     if (cus == 0 && (st = current_num_cus(&cus))) return st;
     const long long units = (long long)d->num_seqs * d->num_kv_heads * row_chunks(d, c, engine);
-    const bool multi_tile =
-        engine == PA_ENGINE_MFMA && !c.multi && pa::mfma_head_tiles(group) > 1;
     const long long target =
-        (long long)(multi_tile ? kTargetGroupsPerCuMultiTile
-                               : engine == PA_ENGINE_VALU ? kTargetGroupsPerCuValu : kTargetGroupsPerCu) *
-        cus;
+        (long long)(engine == PA_ENGINE_VALU ? kTargetGroupsPerCuValu : kTargetGroupsPerCu) * cus;
     const int min_pb = kMinPartitionTokens / d->block_size > 1 ? kMinPartitionTokens / d->block_size : 1;
     if (units > 0 && units < target && maxb > min_pb) {
       long long want = (target + units - 1) / units;
