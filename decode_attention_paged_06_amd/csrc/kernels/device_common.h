@@ -177,7 +177,8 @@ __device__ __forceinline__ uint32_t buffer_load_b32(rsrc_t r, uint32_t off, bool
 // stricter); the issuing wave waits for them with wait_vmcnt and a barrier
 // publishes them to the other waves.  The statements keep their place among
 // the kernel's memory accesses.  M0, which holds the LDS destination, is
-// restored afterwards.
+// restored afterwards; an LDS transfer may not read M0 in the cycle after a
+// scalar write to it (one wait state on this GPU family), hence the s_nop.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ uint32_t lds_address(void* p) {
@@ -186,7 +187,7 @@ __device__ __forceinline__ uint32_t lds_address(void* p) {
 __device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t off, void* dst) {
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\t"
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
       "buffer_load_dwordx4 %1, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(off), "s"(lds_address(dst)), "s"(r)
@@ -195,7 +196,7 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t off, void* dst) {
 __device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t off, void* dst) {
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\t"
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
       "buffer_load_dword %1, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(off), "s"(lds_address(dst)), "s"(r)
