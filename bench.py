@@ -78,7 +78,32 @@ def pages_gib_per_s(num_tokens, num_kv_heads, head_size, elem_bytes, seconds):
     return copy_bytes_once(num_tokens, num_kv_heads, head_size, elem_bytes) / seconds / 2 ** 30
 
 
-def bench_copy(op, steps, warmup, num_tokens):
+def cpu_baseline_copy(op, num_tokens, budget_s):
+    """The oracle's row copy (numpy fancy indexing of raw words) at the same shapes."""
+    import oracle
+    from workloads import gather_inputs, raw_u16
+
+    H, D, BS, NB = 40, 128, 8, 1024
+    g = gather_inputs(num_tokens=num_tokens, num_kv_heads=H, head_size=D, block_size=BS,
+                      num_blocks=NB, dtype="f16", seed=29, device="cpu")
+    kc, vc, slots = raw_u16(g.key_cache), raw_u16(g.value_cache), g.slot_mapping.numpy()
+    rows_k, rows_v = oracle.gather_cached_kv(kc, vc, slots, BS)
+    calls = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        if op == "gather":
+            oracle.gather_cached_kv(kc, vc, slots, BS)
+        else:
+            oracle.kv_cache_write(kc, vc, rows_k, rows_v, slots, BS)
+        calls += 1
+    dt = (time.perf_counter() - t0) / calls
+    moved = 2 * copy_bytes_once(num_tokens, H, D, 2) + 4 * num_tokens
+    return {"value": round(moved / dt / 1e9, 3), "unit": "GB/s read+write", "cores": 1,
+            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "sample": f"{calls} full calls at the same shapes ({dt * 1e3:.1f} ms each, numpy)"}
+
+
+def bench_copy(op, steps, warmup, num_tokens, cpu_seconds=0.0):
     """Time gather_cached_kv or paged_kv_cache_write at the gather page's shapes."""
     import torch
 
@@ -129,13 +154,41 @@ def bench_copy(op, steps, warmup, num_tokens):
                       "GB/s_read_plus_write": round(moved / sec / 1e9, 2),
                       "pct_of_hbm_peak": round(100 * moved / sec / 1e9 / HBM_PEAK_GBPS, 2),
                       "pages_convention_GiB/s": round(pages_gib_per_s(num_tokens, H, D, 2, sec), 2),
-                      "input_sets_rotated": len(sets)}), flush=True)
+                      "input_sets_rotated": len(sets),
+                      **({"cpu_baseline": cpu_baseline_copy(op, num_tokens, cpu_seconds)}
+                         if cpu_seconds > 0 else {})}), flush=True)
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
 
 
-def bench_prefill(steps, warmup, batch, context, new_tokens, partition_size):
+def cpu_baseline_prefill(context, new_tokens, budget_s):
+    """The fp64 oracle on a sample of the prefill workload: one sequence's last new tokens."""
+    import oracle
+    from workloads import prefill_inputs, raw_u16
+
+    threads = _blas_threads()
+    flops, rows, t_total = 0, 0, 0.0
+    n = 1
+    while t_total < budget_s and n <= new_tokens:
+        inp, q, qs, _ = prefill_inputs(new_tokens=[n], seed=77, device="cpu", num_seqs=1,
+                                       num_heads=64, num_kv_heads=8, head_size=128, block_size=16,
+                                       dtype="bf16", context_lens=context)
+        t0 = time.perf_counter()
+        oracle.paged_prefill(raw_u16(q), raw_u16(inp.key_cache), raw_u16(inp.value_cache),
+                             inp.block_tables.numpy(), inp.context_lens.numpy(), qs.numpy(),
+                             inp.scale, 16, dtype="bf16")
+        t_total += time.perf_counter() - t0
+        flops += 4 * 64 * 128 * sum(context - n + i + 1 for i in range(n))
+        rows += n
+        n *= 2
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "sample": f"{rows} query tokens (chunks of 1, 2, 4, ... new tokens of one sequence of "
+                      f"{context} context tokens, {t_total:.1f} s, fp64 numpy)"}
+
+
+def bench_prefill(steps, warmup, batch, context, new_tokens, partition_size, cpu_seconds=0.0):
     """Time causal multi-query attention: `new_tokens` queries per sequence over a
     `context`-token paged cache (GQA 64/8, D 128, bf16, block 16)."""
     import torch
@@ -171,7 +224,9 @@ def bench_prefill(steps, warmup, batch, context, new_tokens, partition_size):
     print(json.dumps({"op": "prefill", "batch": batch, "context": context,
                       "new_tokens": new_tokens, "us_per_call": round(sec * 1e6, 2),
                       "TFLOP/s": round(flops / sec / 1e12, 2),
-                      "pct_of_mfma_peak": round(100 * flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2)}),
+                      "pct_of_mfma_peak": round(100 * flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
+                      **({"cpu_baseline": cpu_baseline_prefill(context, new_tokens, cpu_seconds)}
+                         if cpu_seconds > 0 else {})}),
           flush=True)
 
 
@@ -228,6 +283,14 @@ def workload_label(name, args):
             f"context {args['context_lens']}" + (", ALiBi" if args.get("alibi") else ""))
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        return 1
+
+
 def cpu_baseline(args, budget_s):
     """The fp64 oracle on a bounded sample of the same workload, on the host cores."""
     import numpy as np
@@ -235,11 +298,7 @@ def cpu_baseline(args, budget_s):
     import oracle
     from workloads import algorithmic_bytes, decode_inputs, raw_u16
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = 1
+    threads = _blas_threads()
     sample_args = dict(args)
     n = min(args["num_seqs"], 64)
     sample_args["num_seqs"] = n
@@ -278,10 +337,11 @@ def main():
         calibrate_copy(a.calibrate_copy, a.steps)
         return
     if a.op == "prefill":
-        bench_prefill(a.steps, a.warmup, a.batch or 4, a.context, a.new_tokens, a.partition_size)
+        bench_prefill(a.steps, a.warmup, a.batch or 4, a.context, a.new_tokens, a.partition_size,
+                      0.0 if a.no_cpu_baseline else min(a.cpu_seconds, 5.0))
         return
     if a.op != "decode":
-        bench_copy(a.op, a.steps, a.warmup, a.tokens)
+        bench_copy(a.op, a.steps, a.warmup, a.tokens, 0.0 if a.no_cpu_baseline else min(a.cpu_seconds, 3.0))
         return
 
     import torch
