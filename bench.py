@@ -99,7 +99,7 @@ def cpu_baseline_copy(op, num_tokens, budget_s):
     dt = (time.perf_counter() - t0) / calls
     moved = 2 * copy_bytes_once(num_tokens, H, D, 2) + 4 * num_tokens
     return {"value": round(moved / dt / 1e9, 3), "unit": "GB/s read+write", "cores": 1,
-            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{calls} full calls at the same shapes ({dt * 1e3:.1f} ms each, numpy)"}
 
 
@@ -183,7 +183,7 @@ def cpu_baseline_prefill(context, new_tokens, budget_s):
         rows += n
         n *= 2
     return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{rows} query tokens (chunks of 1, 2, 4, ... new tokens of one sequence of "
                       f"{context} context tokens, {t_total:.1f} s, fp64 numpy)"}
 
@@ -321,7 +321,7 @@ def cpu_baseline(args, budget_s):
                                num_kv_heads=args["num_kv_heads"], head_size=args["head_size"],
                                block_size=args["block_size"], alibi=bool(args.get("alibi")))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{len(done)} sequence decodes cycling over {n} of the {args['num_seqs']} "
                       f"sequences of the same workload ({dt:.1f} s wall, fp64 numpy)",
             "seconds_per_sequence": round(dt / len(done), 4)}
