@@ -155,7 +155,7 @@ int resolve_engine(const pa_dims* d, const CallShape& c, const pa_opts* o, int* 
 long long row_chunks(const pa_dims* d, const CallShape& c, int engine) {
   const int group = d->num_heads / d->num_kv_heads;
   if (c.multi)
-    return ((long long)c.max_new * group + 16 * pa::kPrefillRowTiles - 1) / (16 * pa::kPrefillRowTiles);
+    return ((long long)c.max_new * group + pa::kPrefillRows - 1) / pa::kPrefillRows;
   if (engine == PA_ENGINE_VALU)
     return (group + pa::valu_heads_per_workgroup(group) - 1) / pa::valu_heads_per_workgroup(group);
   return 1;

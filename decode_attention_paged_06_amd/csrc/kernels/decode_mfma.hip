@@ -12,14 +12,14 @@
 //   S^T[t, g]   = sum_d K[t, d] q[g, d]    v_mfma_f32_16x16x32_{f16,bf16}, D/32 steps
 //   O^T[d, g]  += sum_t V[t, d] P[g, t]     v_mfma_f32_16x16x16_{f16,bf16}, D/16 tiles
 //
-// The workgroup has NT x TG waves: wave w computes head tile w % NT over the
-// 16-row tiles tg, tg + TG, tg + 2 TG, ... of the partition (tg = w / NT), with
-// a two-deep software pipeline (the next tile's K/V loads are in flight while
-// the current tile is processed).  The NT tile-waves of a token group walk
-// the same blocks side by side, so a block's K/V comes from HBM once and the
-// other tiles' reads hit the CU's caches (those loads therefore carry no
-// streaming hint); each wave keeps the register footprint of a single tile.
-// The TG token groups' softmax states are merged at the end.
+// The workgroup has NT x TG waves: wave w computes head tile w % NT (RT
+// consecutive 16-row tiles of query rows for multi-query calls, which share
+// each K/V operand and V regrouping) over the 16-row key tiles tg, tg + TG,
+// tg + 2 TG, ... of the partition (tg = w / NT), with
+// the K/V tiles in flight ahead of the one being processed: in registers (a
+// two-deep software pipeline) when NT = 1, staged once per token group
+// through an LDS ring when the NT tile-waves share every K/V tile.  The TG
+// token groups' softmax states are merged at the end.
 //
 // Register layouts (lane = 16 j + r, r = lane % 16, j = lane / 16):
 //   K operand, step i : lane holds K[t = r][16-byte chunk 4i + j]; the load for
@@ -101,7 +101,7 @@ struct VRow<4> {
   static __device__ __forceinline__ uint32_t word(const T& v, int w) { return w == 0 ? v.x : v.y; }
 };
 
-template <typename Fmt, int D, int NT, int TG, bool KV8>
+template <typename Fmt, int D, int NT, int TG, int RT, bool KV8>
 __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeArgs a) {
   // Cache blocks of BS tokens are walked as tiles of TT = min(16, BS) rows, one
   // M = 16 MFMA tile each: a block of 32..256 tokens is BS/16 tiles sharing one
@@ -131,7 +131,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   constexpr int kStageBytes = NK * KPiece::kBytes + 4 * VPiece::kBytes;
   constexpr int kTransfers = NK * KPiece::kTransfers + 4 * VPiece::kTransfers;  // per tile
   constexpr int kRingBytes = STAGE ? TG * kRing * kStageBytes : 0;
-  constexpr int kMergeBytes = TG > 1 ? NT * (EPL * 64 * 16 + 2 * 64 * 4) : 0;
+  constexpr int ROWS = NT * RT * 16;  // query rows per workgroup (RT 16-row tiles per wave)
+  constexpr int kMergeBytes = TG > 1 ? NT * RT * (EPL * 64 * 16 + 2 * 64 * 4) : 0;
   constexpr int kWorkBytes = kRingBytes > kMergeBytes ? kRingBytes : (kMergeBytes > 16 ? kMergeBytes : 16);
   // the ring during the tile loop, the token-group merge after it
   __shared__ __align__(16) char work_lds[kWorkBytes];
@@ -148,8 +149,9 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 
   // ---- which query rows this workgroup owns ---------------------------------
   // A row is a (new token i, query head g) pair of one sequence and kv head,
-  // numbered i * G + g; the workgroup owns NT * 16 consecutive rows.  Decode
-  // has one new token per sequence, so its rows are the group's G heads.
+  // numbered i * G + g; the workgroup owns ROWS consecutive rows, RT tiles of
+  // 16 per wave.  Decode has one new token per sequence, so its rows are the
+  // group's G heads.
   const int chunks = a.row_chunks;
   int xi = blockIdx.x, seq = blockIdx.y, part = blockIdx.z;
   if (a.unit_order != nullptr) {  // longest-first schedule over a 1-D grid
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     q_first = a.query_start[seq];
     n_new = a.query_start[seq + 1] - q_first;
   }
-  const int row_base = rc * NT * 16;
+  const int row_base = rc * ROWS;
   const int nrows = n_new * G;
   if (row_base >= nrows) return;  // this sequence has fewer rows
 
@@ -188,9 +190,9 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     blk_first = block_at(tg);
     blk_second = block_at(tg + TG);
   }
-  // ---- shared query load: the owned rows, zero-padded to NT * 16 ----------
-  __shared__ uint4 q_lds[NT * 16 * CH];
-  for (int idx = threadIdx.x; idx < NT * 16 * CH; idx += NTHREADS) {
+  // ---- shared query load: the owned rows, zero-padded to ROWS -------------
+  __shared__ uint4 q_lds[ROWS * CH];
+  for (int idx = threadIdx.x; idx < ROWS * CH; idx += NTHREADS) {
     const int rr = row_base + idx / CH;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (rr < nrows) {
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const int L = min(ctx_len, a.max_blocks_per_seq * BS);
   if (L <= 0) {
     if (single) {  // no context: zero output rows
-      for (int idx = threadIdx.x; idx < NT * 16 * CH; idx += NTHREADS) {
+      for (int idx = threadIdx.x; idx < ROWS * CH; idx += NTHREADS) {
         const int rr = row_base + idx / CH;
         if (rr < nrows) {
           const int ti = rr / G;
@@ -217,35 +219,48 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     return;
   }
   // the owned rows see keys up to the position of the last owned new token
-  const int last_new = min(n_new, (row_base + NT * 16 + G - 1) / G) - 1;
+  const int last_new = min(n_new, (row_base + ROWS + G - 1) / G) - 1;
   const int kend = L - n_new + last_new + 1;
   const int tok0 = part * a.partition_blocks * BS;
   if (tok0 >= kend) return;  // partition past every owned row's keys: nothing to do
   const int tok1 = min(kend, tok0 + a.partition_blocks * BS);
   const int ntiles = (tok1 - tok0 + TT - 1) / TT;  // tiles holding its tokens
 
-  const int row = row_base + tile * 16 + r;  // this lane's row
-  const bool row_ok = row < nrows;
-  const int ti = row / G;                    // its new token
-  const int g = row - ti * G;                // its query head within the group
-  // its position: keys 0 .. pos are visible (padding rows, past the last new
-  // token, get a position past L; their results are never stored)
-  const int pos = L - n_new + ti;
-  // the lowest position among the wave's 16 rows (wave-uniform): tiles that
-  // end at or before it, and are full, need no masking
-  const int pos_lo = L - n_new + (row_base + tile * 16) / G;
+  // This lane's rows: row r of each of the wave's RT row tiles.
+  bool row_ok[RT];
+  int ti[RT], g[RT], pos[RT], pos_lo[RT];
+  uint4 qb[RT][NK];
+  float slope[RT];
   const bool has_alibi = a.alibi != nullptr;
-  uint4 qb[NK];
 #pragma unroll
-  for (int i = 0; i < NK; ++i) qb[i] = q_lds[(tile * 16 + r) * CH + 4 * i + j];
-  const float slope = (a.alibi != nullptr && row_ok) ? a.alibi[h0 + g] * kLog2e : 0.f;
-  // the slope's load completes here, before the tile loop's own memory traffic
-  asm volatile("" ::"v"(slope));
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rt_base = row_base + (tile * RT + rt) * 16;
+    const int row = rt_base + r;
+    row_ok[rt] = row < nrows;
+    ti[rt] = row / G;             // its new token
+    g[rt] = row - ti[rt] * G;     // its query head within the group
+    // its position: keys 0 .. pos are visible (padding rows, past the last
+    // new token, get a position past L; their results are never stored)
+    pos[rt] = L - n_new + ti[rt];
+    // the lowest position among the tile's 16 rows (wave-uniform): key tiles
+    // that end at or before it, and are full, need no masking
+    pos_lo[rt] = L - n_new + rt_base / G;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) qb[rt][i] = q_lds[((tile * RT + rt) * 16 + r) * CH + 4 * i + j];
+    slope[rt] = (has_alibi && row_ok[rt]) ? a.alibi[h0 + g[rt]] * kLog2e : 0.f;
+    // the slope's load completes here, before the tile loop's own memory traffic
+    asm volatile("" ::"v"(slope[rt]));
+  }
 
-  float m = kNegBig, lsum = 0.f;
-  f32x4_t acc[EPL];
+  float m[RT], lsum[RT];
+  f32x4_t acc[RT][EPL];
 #pragma unroll
-  for (int t = 0; t < EPL; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = kNegBig;
+    lsum[rt] = 0.f;
+#pragma unroll
+    for (int t = 0; t < EPL; ++t) acc[rt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Byte addressing: a wave-uniform tile base (SGPRs) plus a small unsigned
   // per-lane offset, so every K/V load is one buffer load with a VGPR offset.
@@ -296,45 +311,52 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 #pragma unroll
     for (int i = 0; i < 4; ++i) vv[i] = KS::to16(T.v[i]);
 
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    // scores and weights of each row tile (the K tile is shared)
+    uint2 pk[RT];
 #pragma unroll
-    for (int i = 0; i < NK; ++i) s = Mfma<Fmt>::qk(kk[i], qb[i], s);
-    float x[4];
-    if (valid == 16 && tb + 15 <= pos_lo) {  // every row sees every key of the tile
-      if (has_alibi) {
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          x[v] = fmaf(s[v], a.scale_log2, slope * (float)(tb + 4 * j + v - pos));
+      for (int i = 0; i < NK; ++i) sc = Mfma<Fmt>::qk(kk[i], qb[rt][i], sc);
+      float x[4];
+      if (valid == 16 && tb + 15 <= pos_lo[rt]) {  // every row sees every key of the tile
+        if (has_alibi) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            x[v] = fmaf(sc[v], a.scale_log2, slope[rt] * (float)(tb + 4 * j + v - pos[rt]));
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) x[v] = sc[v] * a.scale_log2;
+        }
       } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) x[v] = s[v] * a.scale_log2;
+        for (int v = 0; v < 4; ++v) {
+          const int t = 4 * j + v;
+          const float z = fmaf(sc[v], a.scale_log2, slope[rt] * (float)(tb + t - pos[rt]));
+          x[v] = (t < valid && tb + t <= pos[rt]) ? z : kNegBig;
+        }
       }
-    } else {
+      // The reference max m moves only when some row's tile max exceeds it
+      // by more than kRescaleSlack (weights then stay below 2^kRescaleSlack):
+      // the rescale of l and the accumulators is rare, and the result is the
+      // same quotient acc / l whichever m it is taken against.
+      const float mx = column_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      if (wave_any(mx > m[rt] + kRescaleSlack)) {
+        const float mn = fmaxf(m[rt], mx);
+        const float alpha = fast_exp2(m[rt] - mn);
+        m[rt] = mn;
+        lsum[rt] *= alpha;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = 4 * j + v;
-        const float z = fmaf(s[v], a.scale_log2, slope * (float)(tb + t - pos));
-        x[v] = (t < valid && tb + t <= pos) ? z : kNegBig;
+        for (int t = 0; t < EPL; ++t) acc[rt][t] *= alpha;
       }
+      const uint32_t p01 = Fmt::pack(fast_exp2(x[0] - m[rt]), fast_exp2(x[1] - m[rt]));
+      const uint32_t p23 = Fmt::pack(fast_exp2(x[2] - m[rt]), fast_exp2(x[3] - m[rt]));
+      pk[rt] = make_uint2(p01, p23);
+      lsum[rt] += (Fmt::lo(p01) + Fmt::hi(p01)) + (Fmt::lo(p23) + Fmt::hi(p23));
     }
-    // The reference max m moves only when some row's tile max exceeds it by
-    // more than kRescaleSlack (weights then stay below 2^kRescaleSlack): the
-    // rescale of l and the accumulators is rare, and the result is the same
-    // quotient acc / l whichever m it is taken against.
-    const float mx = column_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-    if (wave_any(mx > m + kRescaleSlack)) {
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
-      lsum *= alpha;
-#pragma unroll
-      for (int t = 0; t < EPL; ++t) acc[t] *= alpha;
-    }
-    const uint32_t p01 = Fmt::pack(fast_exp2(x[0] - m), fast_exp2(x[1] - m));
-    const uint32_t p23 = Fmt::pack(fast_exp2(x[2] - m), fast_exp2(x[3] - m));
-    const uint2 pk = make_uint2(p01, p23);
-    lsum += (Fmt::lo(p01) + Fmt::hi(p01)) + (Fmt::lo(p23) + Fmt::hi(p23));
 
+    // P.V: the V^T operand of each output tile is regrouped once and serves
+    // every row tile
 #pragma unroll
     for (int t = 0; t < EPL; ++t) {
       const int w = t >> 1;
@@ -342,7 +364,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       const uint32_t a2 = VR::word(vv[2], w), a3 = VR::word(vv[3], w);
       const uint2 vt = (t & 1) ? make_uint2(pack_hi_hi(a0, a1), pack_hi_hi(a2, a3))
                                : make_uint2(pack_lo_lo(a0, a1), pack_lo_lo(a2, a3));
-      acc[t] = Mfma<Fmt>::pv(vt, pk, acc[t]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt][t] = Mfma<Fmt>::pv(vt, pk[rt], acc[rt][t]);
     }
   };
 
@@ -448,74 +471,88 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   }
 
   // ---- complete the per-lane sums over the 4 lane groups -------------------
-  lsum = column_sum4(lsum);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) lsum[rt] = column_sum4(lsum[rt]);
 
   // ---- merge the token groups into group 0 (fixed order: deterministic) ----
   if constexpr (TG > 1) {
     auto mrg_acc = reinterpret_cast<f32x4_t(*)[EPL][64]>(work_lds);
-    auto mrg_m = reinterpret_cast<float(*)[64]>(work_lds + NT * EPL * 64 * 16);
-    auto mrg_l = reinterpret_cast<float(*)[64]>(work_lds + NT * EPL * 64 * 16 + NT * 64 * 4);
+    auto mrg_m = reinterpret_cast<float(*)[64]>(work_lds + NT * RT * EPL * 64 * 16);
+    auto mrg_l = reinterpret_cast<float(*)[64]>(work_lds + NT * RT * EPL * 64 * 16 + NT * RT * 64 * 4);
     for (int k = 1; k < TG; ++k) {
       __syncthreads();
       if (tg == k) {
-        mrg_m[tile][lane] = m;
-        mrg_l[tile][lane] = lsum;
 #pragma unroll
-        for (int t = 0; t < EPL; ++t) mrg_acc[tile][t][lane] = acc[t];
+        for (int rt = 0; rt < RT; ++rt) {
+          const int slot = tile * RT + rt;
+          mrg_m[slot][lane] = m[rt];
+          mrg_l[slot][lane] = lsum[rt];
+#pragma unroll
+          for (int t = 0; t < EPL; ++t) mrg_acc[slot][t][lane] = acc[rt][t];
+        }
       }
       __syncthreads();
       if (tg == 0) {
-        const float mo = mrg_m[tile][lane];
-        const float mn = fmaxf(m, mo);
-        const float f = fast_exp2(m - mn);
-        const float fo = fast_exp2(mo - mn);
-        lsum = lsum * f + mrg_l[tile][lane] * fo;
 #pragma unroll
-        for (int t = 0; t < EPL; ++t) acc[t] = acc[t] * f + mrg_acc[tile][t][lane] * fo;
-        m = mn;
+        for (int rt = 0; rt < RT; ++rt) {
+          const int slot = tile * RT + rt;
+          const float mo = mrg_m[slot][lane];
+          const float mn = fmaxf(m[rt], mo);
+          const float f = fast_exp2(m[rt] - mn);
+          const float fo = fast_exp2(mo - mn);
+          lsum[rt] = lsum[rt] * f + mrg_l[slot][lane] * fo;
+#pragma unroll
+          for (int t = 0; t < EPL; ++t) acc[rt][t] = acc[rt][t] * f + mrg_acc[slot][t][lane] * fo;
+          m[rt] = mn;
+        }
       }
     }
   }
 
   // ---- finalise ---------------------------------------------------------------
-  if (tg != 0 || !row_ok) return;
-  const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
-  const size_t orow_idx = (size_t)(q_first + ti) * a.num_heads + h0 + g;
-  if (single) {
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + orow_idx * D;
+  if (tg != 0) return;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      uint32_t wv[EPL / 2];
+  for (int rt = 0; rt < RT; ++rt) {
+    if (!row_ok[rt]) continue;
+    const float inv = lsum[rt] > 0.f ? a.v_scale / lsum[rt] : 0.f;
+    const size_t orow_idx = (size_t)(q_first + ti[rt]) * a.num_heads + h0 + g[rt];
+    if (single) {
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + orow_idx * D;
 #pragma unroll
-      for (int t = 0; t < EPL; t += 2) wv[t / 2] = Fmt::pack(acc[t][v] * inv, acc[t + 1][v] * inv);
-      VT o;
-      if constexpr (EPL == 8) o = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-      else o = make_uint2(wv[0], wv[1]);
-      *reinterpret_cast<VT*>(orow + EPL * (4 * j + v)) = o;
+      for (int v = 0; v < 4; ++v) {
+        uint32_t wv[EPL / 2];
+#pragma unroll
+        for (int t = 0; t < EPL; t += 2)
+          wv[t / 2] = Fmt::pack(acc[rt][t][v] * inv, acc[rt][t + 1][v] * inv);
+        VT o;
+        if constexpr (EPL == 8) o = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        else o = make_uint2(wv[0], wv[1]);
+        *reinterpret_cast<VT*>(orow + EPL * (4 * j + v)) = o;
+      }
+    } else {
+      const size_t slot = orow_idx * a.num_partitions + part;
+      float* orow = a.ws_o + slot * D;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+#pragma unroll
+        for (int t = 0; t < EPL; t += 4)
+          *reinterpret_cast<float4*>(orow + EPL * (4 * j + v) + t) =
+              make_float4(acc[rt][t][v] * inv, acc[rt][t + 1][v] * inv, acc[rt][t + 2][v] * inv,
+                          acc[rt][t + 3][v] * inv);
+      }
+      if (j == 0) reinterpret_cast<float2*>(a.ws_ml)[slot] = make_float2(m[rt], lsum[rt]);
     }
-  } else {
-    const size_t slot = orow_idx * a.num_partitions + part;
-    float* orow = a.ws_o + slot * D;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-#pragma unroll
-      for (int t = 0; t < EPL; t += 4)
-        *reinterpret_cast<float4*>(orow + EPL * (4 * j + v) + t) =
-            make_float4(acc[t][v] * inv, acc[t + 1][v] * inv, acc[t + 2][v] * inv,
-                        acc[t + 3][v] * inv);
-    }
-    if (j == 0) reinterpret_cast<float2*>(a.ws_ml)[slot] = make_float2(m, lsum);
   }
 }
 
 namespace {
 
-template <typename Fmt, int D, int NT, int TG, bool KV8>
+template <typename Fmt, int D, int NT, int TG, int RT, bool KV8>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid = a.unit_order != nullptr
                        ? dim3(a.num_kv_heads * a.row_chunks * a.num_seqs * a.num_partitions)
                        : dim3(a.num_kv_heads * a.row_chunks, a.num_seqs, a.num_partitions);
-  decode_mfma_kernel<Fmt, D, NT, TG, KV8><<<grid, NT * TG * 64, 0, s>>>(a);
+  decode_mfma_kernel<Fmt, D, NT, TG, RT, KV8><<<grid, NT * TG * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -525,14 +562,15 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
 // MQA ragged batch 256 148 -> 134 us).
 template <typename Fmt, int D, bool KV8>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  // multi-query: 4 row tiles (64 query rows) per workgroup, one wave each,
-  // all walking the same keys
-  if (a.query_start != nullptr) return launch_t<Fmt, D, kPrefillRowTiles, 1, KV8>(a, s);
+  // multi-query: kPrefillWaves waves of kPrefillRowTilesPerWave 16-row tiles
+  // each, all walking the same keys
+  if (a.query_start != nullptr)
+    return launch_t<Fmt, D, kPrefillWaves, 1, kPrefillRowTilesPerWave, KV8>(a, s);
   switch (mfma_head_tiles(a.group)) {
-    case 1: return launch_t<Fmt, D, 1, 4, KV8>(a, s);
-    case 2: return launch_t<Fmt, D, 2, 2, KV8>(a, s);
-    case 3: return launch_t<Fmt, D, 3, 4, KV8>(a, s);
-    default: return launch_t<Fmt, D, 4, 1, KV8>(a, s);
+    case 1: return launch_t<Fmt, D, 1, 4, 1, KV8>(a, s);
+    case 2: return launch_t<Fmt, D, 2, 2, 1, KV8>(a, s);
+    case 3: return launch_t<Fmt, D, 3, 4, 1, KV8>(a, s);
+    default: return launch_t<Fmt, D, 4, 1, 1, KV8>(a, s);
   }
 }
 

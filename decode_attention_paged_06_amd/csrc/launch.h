@@ -50,9 +50,12 @@ struct DecodeArgs {
   const int32_t* unit_order = nullptr;
 };
 
-// Head tiles of the MFMA decode workgroup for a group size, and the query-row
-// tiles of a multi-query workgroup.
-constexpr int kPrefillRowTiles = 4;
+// Multi-query workgroups: kPrefillWaves waves, each computing
+// kPrefillRowTilesPerWave tiles of 16 query rows against every K/V tile it
+// reads (the K/V operands and the V regrouping serve all its row tiles).
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRowTilesPerWave = 2;
+constexpr int kPrefillRows = 16 * kPrefillWaves * kPrefillRowTilesPerWave;  // rows per workgroup
 
 // Query heads per VALU workgroup for a group size (heads that share a kv head
 // are processed in chunks of this many; larger groups use several chunks).
