@@ -15,11 +15,11 @@
 // The workgroup has NT x TG waves: wave w computes head tile w % NT (RT
 // consecutive 16-row tiles of query rows for multi-query calls, which share
 // each K/V operand and V regrouping) over the 16-row key tiles tg, tg + TG,
-// tg + 2 TG, ... of the partition (tg = w / NT), with
-// the K/V tiles in flight ahead of the one being processed: in registers (a
-// two-deep software pipeline) when NT = 1, staged once per token group
-// through an LDS ring when the NT tile-waves share every K/V tile.  The TG
-// token groups' softmax states are merged at the end.
+// tg + 2 TG, ... of the partition (tg = w / NT), with the K/V tiles ahead of
+// the one being processed in flight: in registers (a two-deep software
+// pipeline) when NT = 1, staged once per token group through an LDS ring when
+// the NT tile-waves share every K/V tile.  The TG token groups' softmax states
+// are merged at the end.
 //
 // Register layouts (lane = 16 j + r, r = lane % 16, j = lane / 16):
 //   K operand, step i : lane holds K[t = r][16-byte chunk 4i + j]; the load for
@@ -36,16 +36,18 @@
 //                       (r, j) owns the contiguous output slice
 //                       d in [4 EPL j, 4 EPL (j + 1)) of head r.
 // The contraction index may be any permutation as long as both operands agree,
-// which is what lines these layouts up with coalesced loads and no LDS
-// staging of K or V.
+// which is what lines these layouts up with coalesced loads, with no
+// re-layout of K or V on the way (the LDS ring keeps each lane's bytes where
+// a direct load would have put them).
 //
 // Softmax: fp32 online softmax in log2 units against a reference max per
 // head, shared by the 4 lane groups j (two lane swaps per tile); each lane
 // keeps a partial sum of its own rounded p values.  The reference moves (and
 // l and the accumulators are rescaled) only when a tile's max exceeds it by
-// more than 8, so p stays below 2^8 and the rescale is rare.  P is rounded to the storage type before
-// the P.V product (the matrix cores take 16-bit operands); the sum l uses the
-// same rounded values so the normalisation matches what was accumulated.
+// more than 8, so p stays below 2^8 and the rescale is rare.  P is rounded to
+// the 16-bit compute type before the P.V product (the matrix cores take
+// 16-bit operands); the sum l uses the same rounded values so the
+// normalisation matches what was accumulated.
 //
 // FP8 caches: the tile is loaded as stored (1 byte per element, half the
 // bytes) and converted exactly to the 16-bit compute format when processed;

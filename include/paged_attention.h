@@ -32,9 +32,11 @@
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns without synchronising; outputs are valid once the stream has
  *     reached that point.  The library never reads device memory on the host.
- *   - Return value: PA_OK (0) or one of the PA_ERR_* codes.  A non-zero code
- *     means nothing was enqueued.  pa_last_error() then gives a message for
- *     the calling thread.  No entry point aborts, throws or exits.
+ *   - Return value: PA_OK (0) or one of the PA_ERR_* codes.  Every code but
+ *     PA_ERR_LAUNCH means nothing was enqueued; PA_ERR_LAUNCH (the runtime
+ *     rejected a kernel launch) can follow earlier kernels of the same call
+ *     that were enqueued.  pa_last_error() then gives a message for the
+ *     calling thread.  No entry point aborts, throws or exits.
  *   - Entry points are thread-safe and re-entrant.
  */
 #ifndef PAGED_ATTENTION_H
