@@ -105,30 +105,40 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
   const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
   const uint32_t lane_off = (uint32_t)(rho * D + c * 8) * ES;
-  const uint32_t tile_bytes = (uint32_t)TT * D * ES;
   const int qpos = L - 1;  // position of the query token
 
-  for (int u = wave; u < ntiles; u += kWaves) {
+  // One 16-row tile's K and V as stored.  The buffer bound is the tile's valid
+  // rows: rows past the context end (which may hold anything, NaN included)
+  // read back as zeros, and a tile past the partition end reads nothing, so
+  // every pipeline step issues the same loads and the wait counts stay exact.
+  struct VTile {
+    typename KS::Raw8 k[NLOAD], v[NLOAD];
+  };
+  auto block_of = [&](int u) {  // table entry of tile u (clamped to the partition)
+    return table[(tile0 + min(u, ntiles - 1)) >> tpb_shift];
+  };
+  auto load = [&](VTile& T, int u, int blk) {
     const int ua = tile0 + u;
-    const size_t off = (size_t)table[ua >> tpb_shift] * bstride +
-                       (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
-    const rsrc_t rk = make_rsrc(kbase + off, tile_bytes);
-    const rsrc_t rv = make_rsrc(vbase + off, tile_bytes);
-    typename KS::Raw8 kraw[NLOAD], vraw[NLOAD];
+    const size_t off = (size_t)blk * bstride + (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
+    const uint32_t bytes = u < ntiles ? (uint32_t)min(tok1 - ua * TT, TT) * (D * ES) : 0u;
+    const rsrc_t rk = make_rsrc(kbase + off, bytes);
+    const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i)
-      kraw[i] = KS::template load8<true>(rk, lane_off + (uint32_t)ES * TPL * D * i);
+      T.k[i] = KS::template load8<true>(rk, lane_off + (uint32_t)ES * TPL * D * i);
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i)
-      vraw[i] = KS::template load8<true>(rv, lane_off + (uint32_t)ES * TPL * D * i);
+      T.v[i] = KS::template load8<true>(rv, lane_off + (uint32_t)ES * TPL * D * i);
+  };
+
+  auto process = [&](const VTile& T, int u) {
     uint4 kr[NLOAD], vr[NLOAD];
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
-      kr[i] = KS::to16(kraw[i]);
-      vr[i] = KS::to16(vraw[i]);
+      kr[i] = KS::to16(T.k[i]);
+      vr[i] = KS::to16(T.v[i]);
     }
-
-    const int tb = ua * TT;                // absolute position of the tile's row 0
+    const int tb = (tile0 + u) * TT;       // absolute position of the tile's row 0
     const int valid = min(tok1 - tb, TT);  // rows [0, valid) are context tokens
 
     float x[GT][NLOAD];
@@ -169,9 +179,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
 
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
-      const int row = i * TPL + rho;
-      uint4 w = vr[i];
-      if (row >= valid) w = make_uint4(0, 0, 0, 0);  // slot past the context: may hold NaN
+      const uint4 w = vr[i];  // zeros past the context end (buffer bound)
       const float v[8] = {Fmt::lo(w.x), Fmt::hi(w.x), Fmt::lo(w.y), Fmt::hi(w.y),
                           Fmt::lo(w.z), Fmt::hi(w.z), Fmt::lo(w.w), Fmt::hi(w.w)};
 #pragma unroll
@@ -179,6 +187,29 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(x[g][i], v[e], acc[g][e]);
       }
+    }
+  };
+
+  // Two register tiles in a software pipeline: wave w takes tiles w, w + 4,
+  // ...; the loads of its next tile are in flight while the current one is
+  // processed, and the next table entry is read one load ahead.
+  int u = wave;
+  if (u < ntiles) {
+    VTile ta, tb2;
+    load(ta, u, block_of(u));
+    int blk_next = block_of(u + kWaves);
+    while (true) {
+      const int u1 = u + kWaves;
+      load(tb2, u1, blk_next);
+      blk_next = block_of(u1 + kWaves);
+      process(ta, u);
+      if (u1 >= ntiles) break;
+      const int u2 = u1 + kWaves;
+      load(ta, u2, blk_next);
+      blk_next = block_of(u2 + kWaves);
+      process(tb2, u1);
+      if (u2 >= ntiles) break;
+      u = u2;
     }
   }
 
