@@ -164,8 +164,12 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     seq = unit % a.num_seqs;
     part = unit / a.num_seqs;
   }
-  const int kvh = xi / chunks;
-  const int rc = xi - kvh * chunks;
+  // kv heads vary fastest, and row chunks run from the last one down: with
+  // multi-query rows a later chunk sees more keys (its rows sit later in the
+  // sequence), so the longest work units start first (measured +13..24% on
+  // causal multi-query batches against the ascending order)
+  const int kvh = xi % a.num_kv_heads;
+  const int rc = chunks - 1 - xi / a.num_kv_heads;
   const int G = a.group;
   const int h0 = kvh * G;
   const bool single = a.num_partitions == 1;
