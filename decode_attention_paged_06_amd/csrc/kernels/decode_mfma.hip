@@ -135,8 +135,11 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   constexpr int kRingBytes = STAGE ? TG * kRing * kStageBytes : 0;
   constexpr int ROWS = NT * RT * 16;  // query rows per workgroup (RT 16-row tiles per wave)
   constexpr int kMergeBytes = TG > 1 ? NT * RT * (EPL * 64 * 16 + 2 * 64 * 4) : 0;
-  constexpr int kWorkBytes = kRingBytes > kMergeBytes ? kRingBytes : (kMergeBytes > 16 ? kMergeBytes : 16);
-  // the ring during the tile loop, the token-group merge after it
+  constexpr int kQueryBytes = ROWS * (D / 8) * 16;
+  constexpr int kWorkBytes0 = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
+  constexpr int kWorkBytes = kWorkBytes0 > kQueryBytes ? kWorkBytes0 : kQueryBytes;
+  // the query rows before the tile loop (they move to registers first), the
+  // ring during it, the token-group merge after it
   __shared__ __align__(16) char work_lds[kWorkBytes];
   constexpr int kTableWindow = 512;  // block-table entries held in LDS by the staged loop
   __shared__ int tbl_lds[STAGE ? kTableWindow : 1];
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     blk_second = block_at(tg + TG);
   }
   // ---- shared query load: the owned rows, zero-padded to ROWS -------------
-  __shared__ uint4 q_lds[ROWS * CH];
+  uint4* q_lds = reinterpret_cast<uint4*>(work_lds);
   for (int idx = threadIdx.x; idx < ROWS * CH; idx += NTHREADS) {
     const int rr = row_base + idx / CH;
     uint4 v = make_uint4(0, 0, 0, 0);
