@@ -119,19 +119,27 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   using VT = typename VR::T;
   using KS = KVStore<Fmt, KV8>;                  // cache storage (16-bit or FP8)
   constexpr int ES = KS::kBytes;                 // bytes per cached element
-  using KRaw = typename KS::Raw8;                // 8 cached K elements as loaded
+  using KRaw = typename KS::Raw8;                // 8 cached K elements (one q.K step)
+  // K is read 16 bytes per lane: lane (r, j)'s read il covers row r, bytes
+  // 16 j + 64 il .. + 16, and holds KSTEP q.K steps (dims are assigned to the
+  // steps in that order; the query operand uses the same assignment).  Each
+  // read instruction thus covers 64 contiguous bytes of each of 16 rows.
+  constexpr int KSTEP = KS::kKSteps;
+  constexpr int NKL = NK / KSTEP;                // K reads per tile
   using VRaw = typename std::conditional<EPL == 8, typename KS::Raw8, typename KS::Raw4>::type;
   constexpr float kLog2e = 1.4426950408889634f;
   constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay below 256
-  constexpr int kDepth = 2;  // register tiles in the load pipeline (one wave per tile)
+  // register tiles in the load pipeline (one wave per tile); FP8 tiles are half
+  // the size, and a third one in flight measured ~1% faster
+  constexpr int kDepth = KV8 ? 3 : 2;
   // With several head tiles the NT waves of a token group need the same K/V
   // tile: it is staged once through a ring of kRing LDS slots instead.
   constexpr bool STAGE = NT > 1;
   constexpr int kRing = 4;
-  using KPiece = LdsPiece<KRaw>;
+  using KPiece = LdsPiece<uint4>;
   using VPiece = LdsPiece<VRaw>;
-  constexpr int kStageBytes = NK * KPiece::kBytes + 4 * VPiece::kBytes;
-  constexpr int kTransfers = NK * KPiece::kTransfers + 4 * VPiece::kTransfers;  // per tile
+  constexpr int kStageBytes = NKL * KPiece::kBytes + 4 * VPiece::kBytes;
+  constexpr int kTransfers = NKL * KPiece::kTransfers + 4 * VPiece::kTransfers;  // per tile
   constexpr int kRingBytes = STAGE ? TG * kRing * kStageBytes : 0;
   constexpr int ROWS = NT * RT * 16;  // query rows per workgroup (RT 16-row tiles per wave)
   constexpr int kMergeBytes = TG > 1 ? NT * RT * (EPL * 64 * 16 + 2 * 64 * 4) : 0;
@@ -255,7 +263,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     // that end at or before it, and are full, need no masking
     pos_lo[rt] = L - n_new + rt_base / G;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) qb[rt][i] = q_lds[((tile * RT + rt) * 16 + r) * CH + 4 * i + j];
+    for (int i = 0; i < NK; ++i)
+      qb[rt][i] = q_lds[((tile * RT + rt) * 16 + r) * CH + (i / KSTEP) * 4 * KSTEP + j * KSTEP + i % KSTEP];
     slope[rt] = (has_alibi && row_ok[rt]) ? a.alibi[h0 + g[rt]] * kLog2e : 0.f;
     // the slope's load completes here, before the tile loop's own memory traffic
     asm volatile("" ::"v"(slope[rt]));
@@ -277,7 +286,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const size_t head_off = (size_t)kvh * BS * D * ES;
   const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
-  const uint32_t k_lane = (uint32_t)(r * D + j * 8) * ES;          // step-0 K chunk
+  const uint32_t k_lane = (uint32_t)(r * D * ES + j * 16);         // read-0 K chunk
   const uint32_t v_lane = (uint32_t)((4 * j) * D + r * EPL) * ES;  // load-0 V slice
 
   // One 16-row tile's K and V in registers, as stored in the cache.
@@ -300,8 +309,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     const rsrc_t rk = make_rsrc(kbase + off, bytes);
     const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
-    for (int i = 0; i < NK; ++i)
-      T.k[i] = KS::template load8<NT == 1>(rk, k_lane + 32u * ES * i);
+    for (int i = 0; i < NKL; ++i)
+      KS::split(buffer_load<NT == 1>(rk, k_lane + 64u * i, (uint4*)nullptr), &T.k[i * KSTEP]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (EPL == 8) T.v[i] = KS::template load8<NT == 1>(rv, v_lane + (uint32_t)D * ES * i);
@@ -440,17 +449,17 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       const rsrc_t rv = make_rsrc(vbase + off, bytes);
       char* dst = ring + slot * kStageBytes;
 #pragma unroll
-      for (int i = 0; i < NK; ++i) KPiece::copy(rk, k_lane + 32u * ES * i, dst + i * KPiece::kBytes);
+      for (int i = 0; i < NKL; ++i) KPiece::copy(rk, k_lane + 64u * i, dst + i * KPiece::kBytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        VPiece::copy(rv, v_lane + (uint32_t)D * ES * i, dst + NK * KPiece::kBytes + i * VPiece::kBytes);
+        VPiece::copy(rv, v_lane + (uint32_t)D * ES * i, dst + NKL * KPiece::kBytes + i * VPiece::kBytes);
     };
     auto read = [&](Tile& T, int slot) {
       const char* src = ring + slot * kStageBytes;
 #pragma unroll
-      for (int i = 0; i < NK; ++i) T.k[i] = KPiece::read(src + i * KPiece::kBytes, lane);
+      for (int i = 0; i < NKL; ++i) KS::split(KPiece::read(src + i * KPiece::kBytes, lane), &T.k[i * KSTEP]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) T.v[i] = VPiece::read(src + NK * KPiece::kBytes + i * VPiece::kBytes, lane);
+      for (int i = 0; i < 4; ++i) T.v[i] = VPiece::read(src + NKL * KPiece::kBytes + i * VPiece::kBytes, lane);
     };
     const int nsteps = (ntiles + TG - 1) / TG;
     if (issuer) {

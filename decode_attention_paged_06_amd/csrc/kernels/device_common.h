@@ -269,11 +269,16 @@ __device__ __forceinline__ uint32_t fp8x2_to(uint32_t w) {
 
 // How a cache stores 8 (or 4) consecutive elements of a row and how they become
 // the 16-bit compute format.  Native caches hold the compute format already.
+// K rows are read 16 bytes per lane; kKSteps is the number of 8-element q.K
+// operands one such read holds (1 for 16-bit caches, 2 for FP8), and split()
+// hands them out.
 template <typename Fmt, bool FP8>
 struct KVStore {
   static constexpr int kBytes = 2;  // bytes per element
+  static constexpr int kKSteps = 1;
   using Raw8 = uint4;
   using Raw4 = uint2;
+  static __device__ __forceinline__ void split(uint4 w, Raw8* k) { k[0] = w; }
   static __device__ __forceinline__ uint4 to16(uint4 r) { return r; }
   static __device__ __forceinline__ uint2 to16(uint2 r) { return r; }
   template <bool STREAM>
@@ -289,8 +294,13 @@ struct KVStore {
 template <typename Fmt>
 struct KVStore<Fmt, true> {
   static constexpr int kBytes = 1;
+  static constexpr int kKSteps = 2;
   using Raw8 = uint2;
   using Raw4 = uint32_t;
+  static __device__ __forceinline__ void split(uint4 w, Raw8* k) {
+    k[0] = make_uint2(w.x, w.y);
+    k[1] = make_uint2(w.z, w.w);
+  }
   static __device__ __forceinline__ uint4 to16(uint2 r) {
     return make_uint4(fp8x2_to<Fmt, false>(r.x), fp8x2_to<Fmt, true>(r.x),
                       fp8x2_to<Fmt, false>(r.y), fp8x2_to<Fmt, true>(r.y));
