@@ -246,13 +246,16 @@ def calibrate_copy(mib, steps):
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-def recorded_traffic(kernel: str, workload: str, batch: int):
+def recorded_traffic(kernel: str, workload: str, batch: int, kv: str = "native",
+                     block_size: int = 16):
     """HBM bytes per launch from a committed rocprofv3 PMC summary, or None.
 
     A summary under profiles/ ends with a JSON record of the scaled
     FETCH_SIZE + WRITE_SIZE traffic and a SHA-256 of the kernel's sources at
-    the time the counters were taken; the figure is used only while the
-    sources still hash the same.
+    the time the counters were taken; the figure is used only for the same
+    workload, batch, cache format and block size (a record without the last
+    two is of a 16-bit cache with 16-token blocks), and only while the sources
+    still hash the same.
     """
     import glob
     import hashlib
@@ -264,7 +267,8 @@ def recorded_traffic(kernel: str, workload: str, batch: int):
                 continue
             rec = json.loads(line)
             if (kernel not in rec["kernel"] or rec["workload"] != workload
-                    or rec["batch"] != batch):
+                    or rec["batch"] != batch or rec.get("kv", "native") != kv
+                    or rec.get("block_size", 16) != block_size):
                 continue
             h = hashlib.sha256()
             try:
@@ -280,7 +284,8 @@ def recorded_traffic(kernel: str, workload: str, batch: int):
 def workload_label(name, args):
     return (f"{name}: {args['num_heads']}q/{args['num_kv_heads']}kv heads, D={args['head_size']}, "
             f"{args['dtype']}, block {args['block_size']}, batch {args['num_seqs']}, "
-            f"context {args['context_lens']}" + (", ALiBi" if args.get("alibi") else ""))
+            f"context {args['context_lens']}" + (", ALiBi" if args.get("alibi") else "")
+            + (f", {args['kv_dtype']} KV cache" if args.get("kv_dtype") else ""))
 
 
 def _blas_threads():
@@ -473,6 +478,7 @@ def main():
             "workload": workload_label(name, args),
             "num_seqs": batch, "num_heads": args["num_heads"], "num_kv_heads": args["num_kv_heads"],
             "head_size": args["head_size"], "block_size": args["block_size"],
+            "kv_cache": args.get("kv_dtype") or args["dtype"],
             "context_lens": str(args["context_lens"]), "seed": args["seed"],
             "engine": {0: "auto", 1: "valu", 2: "mfma"}[plan.engine] if a.engine == "auto" else a.engine,
             "num_partitions": plan.num_partitions, "partition_size": plan.partition_size,
@@ -488,7 +494,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": recorded_traffic(kernel_name, name, batch),
+            "traffic": recorded_traffic(kernel_name, name, batch, a.kv_dtype or "native",
+                                        args["block_size"]),
             "kernel": kernel_name,
             "kernel_avg_us": round(avg_ms * 1e3, 2),
             "flops_per_call": flops,

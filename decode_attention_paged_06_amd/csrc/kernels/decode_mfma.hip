@@ -22,9 +22,11 @@
 // are merged at the end.
 //
 // Register layouts (lane = 16 j + r, r = lane % 16, j = lane / 16):
-//   K operand, step i : lane holds K[t = r][16-byte chunk 4i + j]; the load for
-//                       step i reads 64 contiguous bytes of each of the 16 rows.
-//   q operand, step i : lane holds q[g = r][chunk 4i + j]   (same k order as K).
+//   K operand, step i : lane holds K[t = r][8-element chunk c(i, j)], where
+//                       c = 4i + j for 16-bit caches and 8(i/2) + 2j + i%2 for
+//                       FP8 (one 16-byte read holds two steps); each read
+//                       covers 64 contiguous bytes of each of the 16 rows.
+//   q operand, step i : lane holds q[g = r][chunk c(i, j)]   (same k order as K).
 //   scores            : lane holds S^T[t = 4j + v][g = r], v = 0..3.
 //   V loads i = 0..3  : lane holds V[t = 4j + i][EPL elements at r * EPL]; each
 //                       load reads 4 whole rows, fully coalesced.
@@ -37,8 +39,8 @@
 //                       d in [4 EPL j, 4 EPL (j + 1)) of head r.
 // The contraction index may be any permutation as long as both operands agree,
 // which is what lines these layouts up with coalesced loads, with no
-// re-layout of K or V on the way (the LDS ring keeps each lane's bytes where
-// a direct load would have put them).
+// re-layout of K or V on the way (a wave reading the LDS ring gets each
+// lane's bytes as a direct load would have).
 //
 // Softmax: fp32 online softmax in log2 units against a reference max per
 // head, shared by the 4 lane groups j (two lane swaps per tile); each lane
@@ -136,10 +138,12 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   // tile: it is staged once through a ring of kRing LDS slots instead.
   constexpr bool STAGE = NT > 1;
   constexpr int kRing = 4;
-  using KPiece = LdsPiece<uint4>;
-  using VPiece = LdsPiece<VRaw>;
-  constexpr int kStageBytes = NKL * KPiece::kBytes + 4 * VPiece::kBytes;
-  constexpr int kTransfers = NKL * KPiece::kTransfers + 4 * VPiece::kTransfers;  // per tile
+  // A staged tile: K as per-lane 16-byte pieces, V as the tile's own 16 rows
+  // (contiguous in the cache), read back at the direct-load offsets.
+  using KPiece = LdsPiece;
+  constexpr int kVBytes = 16 * D * ES;
+  constexpr int kStageBytes = NKL * KPiece::kBytes + kVBytes;
+  constexpr int kTransfers = NKL * KPiece::kTransfers + kVBytes / 1024;  // per tile
   constexpr int kRingBytes = STAGE ? TG * kRing * kStageBytes : 0;
   constexpr int ROWS = NT * RT * 16;  // query rows per workgroup (RT 16-row tiles per wave)
   constexpr int kMergeBytes = TG > 1 ? NT * RT * (EPL * 64 * 16 + 2 * 64 * 4) : 0;
@@ -450,16 +454,15 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       char* dst = ring + slot * kStageBytes;
 #pragma unroll
       for (int i = 0; i < NKL; ++i) KPiece::copy(rk, k_lane + 64u * i, dst + i * KPiece::kBytes);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        VPiece::copy(rv, v_lane + (uint32_t)D * ES * i, dst + NKL * KPiece::kBytes + i * VPiece::kBytes);
+      lds_copy_run<kVBytes>(rv, dst + NKL * KPiece::kBytes, lane);
     };
     auto read = [&](Tile& T, int slot) {
       const char* src = ring + slot * kStageBytes;
 #pragma unroll
       for (int i = 0; i < NKL; ++i) KS::split(KPiece::read(src + i * KPiece::kBytes, lane), &T.k[i * KSTEP]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) T.v[i] = VPiece::read(src + NKL * KPiece::kBytes + i * VPiece::kBytes, lane);
+      for (int i = 0; i < 4; ++i)
+        T.v[i] = *reinterpret_cast<const VRaw*>(src + NKL * KPiece::kBytes + v_lane + (uint32_t)D * ES * i);
     };
     const int nsteps = (ntiles + TG - 1) / TG;
     if (issuer) {

@@ -165,12 +165,13 @@ __device__ __forceinline__ uint32_t buffer_load_b32(rsrc_t r, uint32_t off, bool
 
 // ---- LDS staging ----------------------------------------------------------------
 //
-// A per-lane piece of 16, 8 or 4 bytes is copied from a buffer straight into
-// LDS by the buffer-load-to-LDS instruction: one 16-byte transfer (lane l
-// lands at +16 l) or one 4-byte transfer per word (lane l at +4 l, one
-// 256-byte run per word).  A wave that reads the piece back from the same lane
-// positions gets what a direct load would have given it; past the buffer bound
-// the transfer writes zeros.  The LDS destination must be wave-uniform.
+// Buffer bytes are copied straight into LDS by the buffer-load-to-LDS
+// instruction, 16 bytes per lane: lane l's bytes land at +16 l from the
+// wave-uniform LDS destination; past the buffer bound the transfer writes
+// zeros.  Two uses: a per-lane 16-byte piece (LdsPiece: a wave reading it back
+// from the same lane position gets what a direct load would have given it),
+// and a whole contiguous run copied as is (lds_copy_run: 1 KB per transfer,
+// read back at the offsets a direct load would have used).
 //
 // The transfers are issued from inline assembly, so the compiler does not
 // count them when it places its own waits (which only makes those waits
@@ -193,20 +194,8 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t off, void* dst) {
       : "v"(off), "s"(lds_address(dst)), "s"(r)
       : "memory");
 }
-__device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t off, void* dst) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-      "buffer_load_dword %1, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(lds_address(dst)), "s"(r)
-      : "memory");
-}
 
-template <typename Raw>
-struct LdsPiece;
-template <>
-struct LdsPiece<uint4> {
+struct LdsPiece {
   static constexpr int kTransfers = 1;
   static constexpr int kBytes = 64 * 16;
   static __device__ __forceinline__ void copy(rsrc_t r, uint32_t off, char* dst) {
@@ -216,30 +205,15 @@ struct LdsPiece<uint4> {
     return *reinterpret_cast<const uint4*>(src + 16 * lane);
   }
 };
-template <>
-struct LdsPiece<uint2> {
-  static constexpr int kTransfers = 2;
-  static constexpr int kBytes = 64 * 8;
-  static __device__ __forceinline__ void copy(rsrc_t r, uint32_t off, char* dst) {
-    lds_load4(r, off, dst);
-    lds_load4(r, off + 4, dst + 256);
-  }
-  static __device__ __forceinline__ uint2 read(const char* src, int lane) {
-    return make_uint2(*reinterpret_cast<const uint32_t*>(src + 4 * lane),
-                      *reinterpret_cast<const uint32_t*>(src + 256 + 4 * lane));
-  }
-};
-template <>
-struct LdsPiece<uint32_t> {
-  static constexpr int kTransfers = 1;
-  static constexpr int kBytes = 64 * 4;
-  static __device__ __forceinline__ void copy(rsrc_t r, uint32_t off, char* dst) {
-    lds_load4(r, off, dst);
-  }
-  static __device__ __forceinline__ uint32_t read(const char* src, int lane) {
-    return *reinterpret_cast<const uint32_t*>(src + 4 * lane);
-  }
-};
+
+// Bytes 0 .. BYTES - 1 of the buffer to dst (BYTES a multiple of 1 KB; one
+// transfer per KB).
+template <int BYTES>
+__device__ __forceinline__ void lds_copy_run(rsrc_t r, char* dst, int lane) {
+  static_assert(BYTES % 1024 == 0, "whole transfers");
+#pragma unroll
+  for (int c = 0; c < BYTES / 1024; ++c) lds_load16(r, 1024u * c + 16u * lane, dst + 1024 * c);
+}
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
