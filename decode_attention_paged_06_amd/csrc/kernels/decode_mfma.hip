@@ -340,12 +340,20 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NK; ++i) sc = Mfma<Fmt>::qk(kk[i], qb[rt][i], sc);
+      // x: the tile's logits in log2 units, or (full tile, no ALiBi, positive
+      // scale) the raw scores, with the scale applied in the exponent below;
+      // xs is what x is multiplied by to get the logit
       float x[4];
+      float xs = 1.f;
       if (valid == 16 && tb + 15 <= pos_lo[rt]) {  // every row sees every key of the tile
         if (has_alibi) {
+          const float base = slope[rt] * (float)(tb + 4 * j - pos[rt]);
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            x[v] = fmaf(sc[v], a.scale_log2, slope[rt] * (float)(tb + 4 * j + v - pos[rt]));
+          for (int v = 0; v < 4; ++v) x[v] = fmaf(sc[v], a.scale_log2, fmaf((float)v, slope[rt], base));
+        } else if (a.scale_log2 > 0.f) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) x[v] = sc[v];
+          xs = a.scale_log2;
         } else {
 #pragma unroll
           for (int v = 0; v < 4; ++v) x[v] = sc[v] * a.scale_log2;
@@ -362,7 +370,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       // by more than kRescaleSlack (weights then stay below 2^kRescaleSlack):
       // the rescale of l and the accumulators is rare, and the result is the
       // same quotient acc / l whichever m it is taken against.
-      const float mx = column_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      const float mx = xs * column_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
       if (wave_any(mx > m[rt] + kRescaleSlack)) {
         const float mn = fmaxf(m[rt], mx);
         const float alpha = fast_exp2(m[rt] - mn);
@@ -371,10 +379,12 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 #pragma unroll
         for (int t = 0; t < EPL; ++t) acc[rt][t] *= alpha;
       }
-      const uint32_t p01 = Fmt::pack(fast_exp2(x[0] - m[rt]), fast_exp2(x[1] - m[rt]));
-      const uint32_t p23 = Fmt::pack(fast_exp2(x[2] - m[rt]), fast_exp2(x[3] - m[rt]));
+      const float nm = -m[rt];
+      const uint32_t p01 = Fmt::pack(fast_exp2(fmaf(x[0], xs, nm)), fast_exp2(fmaf(x[1], xs, nm)));
+      const uint32_t p23 = Fmt::pack(fast_exp2(fmaf(x[2], xs, nm)), fast_exp2(fmaf(x[3], xs, nm)));
       pk[rt] = make_uint2(p01, p23);
-      lsum[rt] += (Fmt::lo(p01) + Fmt::hi(p01)) + (Fmt::lo(p23) + Fmt::hi(p23));
+      // l sums the rounded weights that P.V uses (products by one are exact)
+      lsum[rt] = Fmt::dot2(p23, Fmt::kOnes, Fmt::dot2(p01, Fmt::kOnes, lsum[rt]));
     }
 
     // P.V: the V^T operand of each output tile is regrouped once and serves

@@ -27,6 +27,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // ---- 16-bit storage formats -------------------------------------------------
 
 struct F16 {
+  static constexpr uint32_t kOnes = 0x3C003C00u;  // (1, 1) packed
   // value of the low / high half of a packed pair
   static __device__ __forceinline__ float lo(uint32_t u) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
@@ -47,6 +48,7 @@ struct F16 {
 };
 
 struct BF16 {
+  static constexpr uint32_t kOnes = 0x3F803F80u;  // (1, 1) packed
   static __device__ __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
   static __device__ __forceinline__ float hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
   static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
