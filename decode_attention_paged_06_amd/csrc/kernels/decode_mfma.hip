@@ -75,6 +75,9 @@ struct Mfma<F16> {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
                                                  __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4_t pv(uint4 a, uint4 b, f32x4_t c) {  // 32 keys
+    return qk(a, b, c);
+  }
 };
 
 template <>
@@ -86,6 +89,9 @@ struct Mfma<BF16> {
   static __device__ __forceinline__ f32x4_t pv(uint2 a, uint2 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
                                                      __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(uint4 a, uint4 b, f32x4_t c) {  // 32 keys
+    return qk(a, b, c);
   }
 };
 
@@ -105,7 +111,7 @@ struct VRow<4> {
   static __device__ __forceinline__ uint32_t word(const T& v, int w) { return w == 0 ? v.x : v.y; }
 };
 
-template <typename Fmt, int D, int NT, int TG, int RT, bool KV8>
+template <typename Fmt, int D, int NT, int TG, int RT, int KT, bool KV8>
 __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeArgs a) {
   // Cache blocks of BS tokens are walked as tiles of TT = min(16, BS) rows, one
   // M = 16 MFMA tile each: a block of 32..256 tokens is BS/16 tiles sharing one
@@ -137,14 +143,18 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   // With several head tiles the NT waves of a token group need the same K/V
   // tile: it is staged once through a ring of kRing LDS slots instead.
   constexpr bool STAGE = NT > 1;
-  constexpr int kRing = 4;
+  // KT = 2: the LDS ring holds pairs of consecutive tiles, processed together
+  // (one softmax max per 32 keys; P.V on the 32-deep MFMA, whose two operands
+  // are the two tiles' 16-key operands side by side)
+  static_assert(KT == 1 || (KT == 2 && STAGE), "tile pairs are staged");
+  constexpr int kRing = KT == 2 ? 3 : 4;  // ring slots (of KT tiles)
   // A staged tile: K as per-lane 16-byte pieces, V as the tile's own 16 rows
   // (contiguous in the cache), read back at the direct-load offsets.
   using KPiece = LdsPiece;
   constexpr int kVBytes = 16 * D * ES;
   constexpr int kStageBytes = NKL * KPiece::kBytes + kVBytes;
   constexpr int kTransfers = NKL * KPiece::kTransfers + kVBytes / 1024;  // per tile
-  constexpr int kRingBytes = STAGE ? TG * kRing * kStageBytes : 0;
+  constexpr int kRingBytes = STAGE ? TG * kRing * KT * kStageBytes : 0;
   constexpr int ROWS = NT * RT * 16;  // query rows per workgroup (RT 16-row tiles per wave)
   constexpr int kMergeBytes = TG > 1 ? NT * RT * (EPL * 64 * 16 + 2 * 64 * 4) : 0;
   constexpr int kQueryBytes = ROWS * (D / 8) * 16;
@@ -322,55 +332,66 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     }
   };
 
-  auto process = [&](Tile& T, int u) {
-    const int tb = (tile0 + u) * TT;       // absolute position of the tile's row 0
-    const int valid = min(tok1 - tb, TT);  // rows [0, valid) are context tokens
-    // the compute format of the tile (a no-op for 16-bit caches)
-    uint4 kk[NK];
-    VT vv[4];
+  // T: KT consecutive tiles u0, u0 + 1, ...
+  auto process = [&](const Tile* T, int u0) {
+    // the compute format of the tiles (a no-op for 16-bit caches)
+    uint4 kk[KT][NK];
+    VT vv[KT][4];
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kk[i] = KS::to16(T.k[i]);
+    for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vv[i] = KS::to16(T.v[i]);
+      for (int i = 0; i < NK; ++i) kk[kt][i] = KS::to16(T[kt].k[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[kt][i] = KS::to16(T[kt].v[i]);
+    }
 
-    // scores and weights of each row tile (the K tile is shared)
-    uint2 pk[RT];
+    // scores and weights of each row tile (the K tiles are shared)
+    using PK = typename std::conditional<KT == 2, uint4, uint2>::type;
+    PK pk[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < NK; ++i) sc = Mfma<Fmt>::qk(kk[i], qb[rt][i], sc);
-      // x: the tile's logits in log2 units, or (full tile, no ALiBi, positive
-      // scale) the raw scores, with the scale applied in the exponent below;
+      // x: a tile's logits in log2 units, or (full tile, no ALiBi, positive
+      // scale) its raw scores, with the scale applied in the exponent below;
       // xs is what x is multiplied by to get the logit
-      float x[4];
-      float xs = 1.f;
-      if (valid == 16 && tb + 15 <= pos_lo[rt]) {  // every row sees every key of the tile
-        if (has_alibi) {
-          const float base = slope[rt] * (float)(tb + 4 * j - pos[rt]);
+      float x[KT][4], xs[KT];
+      float local = kNegBig;  // this lane's largest logit
 #pragma unroll
-          for (int v = 0; v < 4; ++v) x[v] = fmaf(sc[v], a.scale_log2, fmaf((float)v, slope[rt], base));
-        } else if (a.scale_log2 > 0.f) {
+      for (int kt = 0; kt < KT; ++kt) {
+        const int tb = (tile0 + u0 + kt) * TT;  // absolute position of the tile's row 0
+        const int valid = min(tok1 - tb, TT);   // rows [0, valid) are context tokens
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int v = 0; v < 4; ++v) x[v] = sc[v];
-          xs = a.scale_log2;
+        for (int i = 0; i < NK; ++i) sc = Mfma<Fmt>::qk(kk[kt][i], qb[rt][i], sc);
+        xs[kt] = 1.f;
+        if (valid == 16 && tb + 15 <= pos_lo[rt]) {  // every row sees every key of the tile
+          if (has_alibi) {
+            const float base = slope[rt] * (float)(tb + 4 * j - pos[rt]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              x[kt][v] = fmaf(sc[v], a.scale_log2, fmaf((float)v, slope[rt], base));
+          } else if (a.scale_log2 > 0.f) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) x[kt][v] = sc[v];
+            xs[kt] = a.scale_log2;
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) x[kt][v] = sc[v] * a.scale_log2;
+          }
         } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) x[v] = sc[v] * a.scale_log2;
+          for (int v = 0; v < 4; ++v) {
+            const int t = 4 * j + v;
+            const float z = fmaf(sc[v], a.scale_log2, slope[rt] * (float)(tb + t - pos[rt]));
+            x[kt][v] = (t < valid && tb + t <= pos[rt]) ? z : kNegBig;
+          }
         }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int t = 4 * j + v;
-          const float z = fmaf(sc[v], a.scale_log2, slope[rt] * (float)(tb + t - pos[rt]));
-          x[v] = (t < valid && tb + t <= pos[rt]) ? z : kNegBig;
-        }
+        local = fmaxf(local, xs[kt] * fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
       }
-      // The reference max m moves only when some row's tile max exceeds it
-      // by more than kRescaleSlack (weights then stay below 2^kRescaleSlack):
-      // the rescale of l and the accumulators is rare, and the result is the
-      // same quotient acc / l whichever m it is taken against.
-      const float mx = xs * column_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      // The reference max m moves only when some row's max over the step
+      // exceeds it by more than kRescaleSlack (weights then stay below
+      // 2^kRescaleSlack): the rescale of l and the accumulators is rare, and
+      // the result is the same quotient acc / l whichever m it is taken against.
+      const float mx = column_max4(local);
       if (wave_any(mx > m[rt] + kRescaleSlack)) {
         const float mn = fmaxf(m[rt], mx);
         const float alpha = fast_exp2(m[rt] - mn);
@@ -380,24 +401,41 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
         for (int t = 0; t < EPL; ++t) acc[rt][t] *= alpha;
       }
       const float nm = -m[rt];
-      const uint32_t p01 = Fmt::pack(fast_exp2(fmaf(x[0], xs, nm)), fast_exp2(fmaf(x[1], xs, nm)));
-      const uint32_t p23 = Fmt::pack(fast_exp2(fmaf(x[2], xs, nm)), fast_exp2(fmaf(x[3], xs, nm)));
-      pk[rt] = make_uint2(p01, p23);
-      // l sums the rounded weights that P.V uses (products by one are exact)
-      lsum[rt] = Fmt::dot2(p23, Fmt::kOnes, Fmt::dot2(p01, Fmt::kOnes, lsum[rt]));
+      uint32_t pw[2 * KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        pw[2 * kt] = Fmt::pack(fast_exp2(fmaf(x[kt][0], xs[kt], nm)), fast_exp2(fmaf(x[kt][1], xs[kt], nm)));
+        pw[2 * kt + 1] =
+            Fmt::pack(fast_exp2(fmaf(x[kt][2], xs[kt], nm)), fast_exp2(fmaf(x[kt][3], xs[kt], nm)));
+        // l sums the rounded weights that P.V uses (products by one are exact)
+        lsum[rt] = Fmt::dot2(pw[2 * kt + 1], Fmt::kOnes, Fmt::dot2(pw[2 * kt], Fmt::kOnes, lsum[rt]));
+      }
+      if constexpr (KT == 2) pk[rt] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      else pk[rt] = make_uint2(pw[0], pw[1]);
     }
 
     // P.V: the V^T operand of each output tile is regrouped once and serves
-    // every row tile
+    // every row tile; with tile pairs the contraction runs over 32 keys, the
+    // first tile's 4 keys of each lane group followed by the second's (the
+    // weights above are laid out the same way)
 #pragma unroll
     for (int t = 0; t < EPL; ++t) {
       const int w = t >> 1;
-      const uint32_t a0 = VR::word(vv[0], w), a1 = VR::word(vv[1], w);
-      const uint32_t a2 = VR::word(vv[2], w), a3 = VR::word(vv[3], w);
-      const uint2 vt = (t & 1) ? make_uint2(pack_hi_hi(a0, a1), pack_hi_hi(a2, a3))
-                               : make_uint2(pack_lo_lo(a0, a1), pack_lo_lo(a2, a3));
+      uint2 vt[KT];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[rt][t] = Mfma<Fmt>::pv(vt, pk[rt], acc[rt][t]);
+      for (int kt = 0; kt < KT; ++kt) {
+        const uint32_t a0 = VR::word(vv[kt][0], w), a1 = VR::word(vv[kt][1], w);
+        const uint32_t a2 = VR::word(vv[kt][2], w), a3 = VR::word(vv[kt][3], w);
+        vt[kt] = (t & 1) ? make_uint2(pack_hi_hi(a0, a1), pack_hi_hi(a2, a3))
+                         : make_uint2(pack_lo_lo(a0, a1), pack_lo_lo(a2, a3));
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if constexpr (KT == 2)
+          acc[rt][t] = Mfma<Fmt>::pv(make_uint4(vt[0].x, vt[0].y, vt[1].x, vt[1].y), pk[rt], acc[rt][t]);
+        else
+          acc[rt][t] = Mfma<Fmt>::pv(vt[0], pk[rt], acc[rt][t]);
+      }
     }
   };
 
@@ -422,7 +460,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
             const int uc = u + k * TG;
             load(buf[(k + kDepth - 1) % kDepth], uc + (kDepth - 1) * TG, blk_next);
             blk_next = block_of(uc + kDepth * TG);
-            process(buf[k], uc);
+            process(&buf[k], uc);
             more = uc + TG < ntiles;
           }
         }
@@ -452,50 +490,58 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     fill_window(0);
     __syncthreads();
 
-    char* ring = work_lds + tg * (kRing * kStageBytes);
+    char* ring = work_lds + tg * (kRing * KT * kStageBytes);
     const bool issuer = tile == 0;
-    auto copy = [&](int u, int slot) {
-      const int ua = tile0 + u;
-      const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[rel_block(u) - win0]);
-      const size_t off = (size_t)blk * bstride + (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
-      const uint32_t bytes = u < ntiles ? (uint32_t)min(tok1 - ua * TT, TT) * (D * ES) : 0u;
-      const rsrc_t rk = make_rsrc(kbase + off, bytes);
-      const rsrc_t rv = make_rsrc(vbase + off, bytes);
-      char* dst = ring + slot * kStageBytes;
+    // ring slots hold KT consecutive tiles: step unit us covers tiles
+    // us KT .. us KT + KT - 1 (those past the partition read nothing)
+    auto copy = [&](int us, int slot) {
 #pragma unroll
-      for (int i = 0; i < NKL; ++i) KPiece::copy(rk, k_lane + 64u * i, dst + i * KPiece::kBytes);
-      lds_copy_run<kVBytes>(rv, dst + NKL * KPiece::kBytes, lane);
+      for (int kt = 0; kt < KT; ++kt) {
+        const int u = us * KT + kt;
+        const int ua = tile0 + u;
+        const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[rel_block(u) - win0]);
+        const size_t off = (size_t)blk * bstride + (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
+        const uint32_t bytes = u < ntiles ? (uint32_t)min(tok1 - ua * TT, TT) * (D * ES) : 0u;
+        const rsrc_t rk = make_rsrc(kbase + off, bytes);
+        const rsrc_t rv = make_rsrc(vbase + off, bytes);
+        char* dst = ring + (slot * KT + kt) * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) KPiece::copy(rk, k_lane + 64u * i, dst + i * KPiece::kBytes);
+        lds_copy_run<kVBytes>(rv, dst + NKL * KPiece::kBytes, lane);
+      }
     };
-    auto read = [&](Tile& T, int slot) {
-      const char* src = ring + slot * kStageBytes;
+    auto read = [&](Tile& T, int slot, int kt) {
+      const char* src = ring + (slot * KT + kt) * kStageBytes;
 #pragma unroll
       for (int i = 0; i < NKL; ++i) KS::split(KPiece::read(src + i * KPiece::kBytes, lane), &T.k[i * KSTEP]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         T.v[i] = *reinterpret_cast<const VRaw*>(src + NKL * KPiece::kBytes + v_lane + (uint32_t)D * ES * i);
     };
-    const int nsteps = (ntiles + TG - 1) / TG;
+    const int nunits = (ntiles + KT - 1) / KT;
+    const int nsteps = (nunits + TG - 1) / TG;
     if (issuer) {
 #pragma unroll
       for (int k = 0; k + 1 < kRing; ++k) copy(tg + k * TG, k);
     }
     for (int j = 0; j < nsteps; ++j) {
-      if (issuer) wait_vmcnt<kTransfers * (kRing - 2)>();  // tile j has landed
-      // the tiles copied in this step are (j + kRing - 1) TG + 0 .. TG - 1
+      if (issuer) wait_vmcnt<kTransfers * KT * (kRing - 2)>();  // unit j has landed
+      // the units copied in this step are (j + kRing - 1) TG + 0 .. TG - 1
       const int first = (j + kRing - 1) * TG;
-      if (rel_block(first + TG - 1) >= win0 + kTableWindow) {  // same for every wave
+      if (rel_block((first + TG) * KT - 1) >= win0 + kTableWindow) {  // same for every wave
         lds_barrier();  // every issuer is done with the old window
-        win0 = rel_block(first);
+        win0 = rel_block(first * KT);
         fill_window(win0);
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       }
-      lds_barrier();  // tile j is visible to every wave; slot (j - 1) % kRing is free
+      lds_barrier();  // unit j is visible to every wave; slot (j - 1) % kRing is free
       if (issuer) copy(tg + first, (j + kRing - 1) % kRing);
       const int uc = tg + j * TG;
-      if (uc < ntiles) {
-        Tile T;
-        read(T, j % kRing);
-        process(T, uc);
+      if (uc < nunits) {
+        Tile T[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) read(T[kt], j % kRing, kt);
+        process(T, uc * KT);
       }
     }
     if (issuer) wait_vmcnt<0>();  // the copies past the end have landed before the LDS is reused
@@ -578,12 +624,12 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 
 namespace {
 
-template <typename Fmt, int D, int NT, int TG, int RT, bool KV8>
+template <typename Fmt, int D, int NT, int TG, int RT, int KT, bool KV8>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid = a.unit_order != nullptr
                        ? dim3(a.num_kv_heads * a.row_chunks * a.num_seqs * a.num_partitions)
                        : dim3(a.num_kv_heads * a.row_chunks, a.num_seqs, a.num_partitions);
-  decode_mfma_kernel<Fmt, D, NT, TG, RT, KV8><<<grid, NT * TG * 64, 0, s>>>(a);
+  decode_mfma_kernel<Fmt, D, NT, TG, RT, KT, KV8><<<grid, NT * TG * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -596,12 +642,12 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   // multi-query: kPrefillWaves waves of kPrefillRowTilesPerWave 16-row tiles
   // each, all walking the same keys
   if (a.query_start != nullptr)
-    return launch_t<Fmt, D, kPrefillWaves, 1, kPrefillRowTilesPerWave, KV8>(a, s);
+    return launch_t<Fmt, D, kPrefillWaves, 1, kPrefillRowTilesPerWave, 2, KV8>(a, s);
   switch (mfma_head_tiles(a.group)) {
-    case 1: return launch_t<Fmt, D, 1, 4, 1, KV8>(a, s);
-    case 2: return launch_t<Fmt, D, 2, 2, 1, KV8>(a, s);
-    case 3: return launch_t<Fmt, D, 3, 4, 1, KV8>(a, s);
-    default: return launch_t<Fmt, D, 4, 1, 1, KV8>(a, s);
+    case 1: return launch_t<Fmt, D, 1, 4, 1, 1, KV8>(a, s);
+    case 2: return launch_t<Fmt, D, 2, 2, 1, 1, KV8>(a, s);
+    case 3: return launch_t<Fmt, D, 3, 4, 1, 1, KV8>(a, s);
+    default: return launch_t<Fmt, D, 4, 1, 1, 1, KV8>(a, s);
   }
 }
 
