@@ -12,13 +12,16 @@
 //   S^T[t, g]   = sum_d K[t, d] q[g, d]    v_mfma_f32_16x16x32_{f16,bf16}, D/32 steps
 //   O^T[d, g]  += sum_t V[t, d] P[g, t]     v_mfma_f32_16x16x16_{f16,bf16}, D/16 tiles
 //
+// (multi-query calls take key tiles in pairs, KT = 2, and run P.V on the
+// 16x16x32 form over the pair's 32 keys).
+//
 // The workgroup has NT x TG waves: wave w computes head tile w % NT (RT
 // consecutive 16-row tiles of query rows for multi-query calls, which share
 // each K/V operand and V regrouping) over the 16-row key tiles tg, tg + TG,
 // tg + 2 TG, ... of the partition (tg = w / NT), with the K/V tiles ahead of
-// the one being processed in flight: in registers (a two-deep software
-// pipeline) when NT = 1, staged once per token group through an LDS ring when
-// the NT tile-waves share every K/V tile.  The TG token groups' softmax states
+// the one being processed in flight: in registers (a software pipeline two
+// tiles deep, three for FP8) when NT = 1, staged once per token group through
+// an LDS ring when the NT tile-waves share every K/V tile.  The TG token groups' softmax states
 // are merged at the end.
 //
 // Register layouts (lane = 16 j + r, r = lane % 16, j = lane / 16):
@@ -43,9 +46,9 @@
 // lane's bytes as a direct load would have).
 //
 // Softmax: fp32 online softmax in log2 units against a reference max per
-// head, shared by the 4 lane groups j (two lane swaps per tile); each lane
+// head, shared by the 4 lane groups j (two lane swaps per step); each lane
 // keeps a partial sum of its own rounded p values.  The reference moves (and
-// l and the accumulators are rescaled) only when a tile's max exceeds it by
+// l and the accumulators are rescaled) only when a step's max exceeds it by
 // more than 8, so p stays below 2^8 and the rescale is rare.  P is rounded to
 // the 16-bit compute type before the P.V product (the matrix cores take
 // 16-bit operands); the sum l uses the same rounded values so the
@@ -636,11 +639,13 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
 // Head tiles NT = ceil(G / 16); token groups TG chosen so a workgroup has
 // 4 waves where possible; 48-head groups (3 tiles sharing every K/V tile
 // through the LDS ring) take 4 token groups, 12 waves (measured against 2:
-// MQA ragged batch 256 148 -> 134 us).
+// MQA ragged batch 256 148 -> 134 us; against 3: 133 -> 126 us).  For one
+// head tile, 1-3 token groups were measured slower or, with one group, unfit
+// for ragged batches (a whole sequence on one wave).
 template <typename Fmt, int D, bool KV8>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   // multi-query: kPrefillWaves waves of kPrefillRowTilesPerWave 16-row tiles
-  // each, all walking the same keys
+  // each, all walking the same keys, in pairs of key tiles
   if (a.query_start != nullptr)
     return launch_t<Fmt, D, kPrefillWaves, 1, kPrefillRowTilesPerWave, 2, KV8>(a, s);
   switch (mfma_head_tiles(a.group)) {

@@ -81,3 +81,18 @@ def test_prefill_empty_sequences_and_chunk():
     ref = ref_prefill(inp, q, qs)
     for ps in (0, 256):
         compare(run_prefill(inp, q, qs, max_q, ps), ref, "bf16", what=f"chunk partition={ps}")
+
+
+def test_prefill_table_window():
+    """A partition longer than the block-table window the staged loop keeps in
+    LDS (512 entries): 8-token blocks, 5000 + tokens of context, one pass."""
+    dev = device()
+    lens = [5000, 4203]
+    news = [37, 6]
+    inp, q, qs, max_q = prefill_inputs(new_tokens=news, seed=13, device=dev, num_seqs=2,
+                                       num_heads=16, num_kv_heads=2, head_size=64,
+                                       block_size=8, dtype="f16", context_lens=lens,
+                                       alibi=True, poison=True)
+    ref = ref_prefill(inp, q, qs)
+    for ps in (-1, 0, 4096):
+        compare(run_prefill(inp, q, qs, max_q, ps), ref, "f16", what=f"window partition={ps}")
