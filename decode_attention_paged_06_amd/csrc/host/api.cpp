@@ -31,15 +31,22 @@ int ok() {
 
 constexpr size_t kWsAlign = 256;
 constexpr int kMaxDevices = 64;
-// Workgroups per CU the auto plan aims for before it splits contexts; the
-// VALU engine less (its split costs more than the grid fill gains on the
-// 40-head MHA batch: 320 workgroups run best as one pass).  For 48-head MQA
-// with ragged lengths (12-wave workgroups) two partitions of 4096 tokens
-// measured best (121 us against 134 with four).
+// Workgroups per CU the auto plan aims for before it splits contexts.  Decode
+// with one head tile (4-wave workgroups): one per CU, in partitions of at
+// least 64 tokens -- fewer, longer partitions measured faster than two per CU
+// (GQA 64/8 context 4096 batch 4: 18.6 -> 17.8 us; context 1024 batch 16:
+// 19.1 -> 18.4 us, batch 1: 8.7 -> 8.3 us).  Several head tiles and
+// multi-query calls: two per CU (48-head MQA with ragged lengths, 12-wave
+// workgroups: two partitions of 4096 tokens measured best, 121 us against 134
+// with four).  The VALU engine: one (its split costs more than the grid fill
+// gains on the 40-head MHA batch: 320 workgroups run best as one pass).
 constexpr int kTargetGroupsPerCu = 2;
+constexpr int kTargetGroupsPerCuOneTile = 1;
 constexpr int kTargetGroupsPerCuValu = 1;
-// Smallest partition the auto plan makes: 128 tokens (two 16-row tiles per wave).
+// Smallest partition the auto plan makes: 128 tokens (two 16-row tiles per
+// wave), 64 for one-head-tile decode.
 constexpr int kMinPartitionTokens = 128;
+constexpr int kMinPartitionTokensOneTile = 64;
 
 std::atomic<int> g_num_cus[kMaxDevices];
 
@@ -201,9 +208,12 @@ int make_plan(const pa_dims* d, const CallShape& c, size_t ws_bytes, const pa_op
     if (cus < 0) return fail(PA_ERR_INVALID_ARG, "num_cus = %d", cus);
     if (cus == 0 && (st = current_num_cus(&cus))) return st;
     const long long units = (long long)d->num_seqs * d->num_kv_heads * row_chunks(d, c, engine);
-    const long long target =
-        (long long)(engine == PA_ENGINE_VALU ? kTargetGroupsPerCuValu : kTargetGroupsPerCu) * cus;
-    const int min_pb = kMinPartitionTokens / d->block_size > 1 ? kMinPartitionTokens / d->block_size : 1;
+    const bool one_tile = engine == PA_ENGINE_MFMA && !c.multi && pa::mfma_head_tiles(group) == 1;
+    const long long target = (long long)(engine == PA_ENGINE_VALU ? kTargetGroupsPerCuValu
+                                         : one_tile                ? kTargetGroupsPerCuOneTile
+                                                                   : kTargetGroupsPerCu) * cus;
+    const int min_tokens = one_tile ? kMinPartitionTokensOneTile : kMinPartitionTokens;
+    const int min_pb = min_tokens / d->block_size > 1 ? min_tokens / d->block_size : 1;
     if (units > 0 && units < target && maxb > min_pb) {
       long long want = (target + units - 1) / units;
       PB = (int)((maxb + want - 1) / want);

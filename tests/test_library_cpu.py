@@ -250,8 +250,20 @@ def test_plan_block_sizes(L):
     for bs, maxb in ((8, 512), (32, 128), (256, 16)):
         st, p = plan(L, dims(S=1, BS=bs, MAXB=maxb))
         assert st == OK and p.num_partitions > 1 and p.partition_size % bs == 0
-        assert p.partition_size >= 128
+        assert p.partition_size >= 64           # one-head-tile decode: 64-token minimum
         assert p.num_partitions * p.partition_size >= maxb * bs
+
+
+def test_plan_one_tile_targets_one_group_per_cu(L):
+    # GQA 64/8 (one 16-head tile): about one workgroup per CU, partitions of
+    # 64+ tokens; 256 CUs
+    for S, maxb, P in ((1, 256, 32), (4, 256, 8), (16, 256, 2), (1, 64, 16), (4, 64, 8),
+                       (16, 64, 2), (64, 256, 1)):
+        st, p = plan(L, dims(S=S, MAXB=maxb))
+        assert st == OK and p.engine == 2 and p.num_partitions == P, (S, maxb, p.num_partitions)
+    # a 48-head group (three tiles) keeps two workgroups per CU
+    st, p = plan(L, dims(S=64, Hq=48, Hkv=1, MAXB=256))
+    assert st == OK and p.num_partitions == 8
 
 
 def test_plan_multi_tile_partitions(L):
