@@ -162,10 +162,10 @@ def bench_copy(op, steps, warmup, num_tokens, cpu_seconds=0.0):
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
 
 
-def cpu_baseline_prefill(context, new_tokens, budget_s):
+def cpu_baseline_prefill(context, new_tokens, budget_s, kv_dtype=None):
     """The fp64 oracle on a sample of the prefill workload: one sequence's last new tokens."""
     import oracle
-    from workloads import prefill_inputs, raw_u16
+    from workloads import prefill_inputs, raw_bits, raw_u16
 
     threads = _blas_threads()
     flops, rows, t_total = 0, 0, 0.0
@@ -173,11 +173,11 @@ def cpu_baseline_prefill(context, new_tokens, budget_s):
     while t_total < budget_s and n <= new_tokens:
         inp, q, qs, _ = prefill_inputs(new_tokens=[n], seed=77, device="cpu", num_seqs=1,
                                        num_heads=64, num_kv_heads=8, head_size=128, block_size=16,
-                                       dtype="bf16", context_lens=context)
+                                       dtype="bf16", context_lens=context, kv_dtype=kv_dtype)
         t0 = time.perf_counter()
-        oracle.paged_prefill(raw_u16(q), raw_u16(inp.key_cache), raw_u16(inp.value_cache),
+        oracle.paged_prefill(raw_u16(q), raw_bits(inp.key_cache), raw_bits(inp.value_cache),
                              inp.block_tables.numpy(), inp.context_lens.numpy(), qs.numpy(),
-                             inp.scale, 16, dtype="bf16")
+                             inp.scale, 16, dtype="bf16", k_scale=inp.k_scale, v_scale=inp.v_scale)
         t_total += time.perf_counter() - t0
         flops += 4 * 64 * 128 * sum(context - n + i + 1 for i in range(n))
         rows += n
@@ -188,9 +188,11 @@ def cpu_baseline_prefill(context, new_tokens, budget_s):
                       f"{context} context tokens, {t_total:.1f} s, fp64 numpy)"}
 
 
-def bench_prefill(steps, warmup, batch, context, new_tokens, partition_size, cpu_seconds=0.0):
+def bench_prefill(steps, warmup, batch, context, new_tokens, partition_size, cpu_seconds=0.0,
+                  kv_dtype=None):
     """Time causal multi-query attention: `new_tokens` queries per sequence over a
-    `context`-token paged cache (GQA 64/8, D 128, bf16, block 16)."""
+    `context`-token paged cache (GQA 64/8, D 128, bf16, block 16; FP8 E4M3 cache
+    with kv_dtype="fp8")."""
     import torch
 
     from decode_attention_paged_06_amd import paged_attention_prefill
@@ -200,13 +202,14 @@ def bench_prefill(steps, warmup, batch, context, new_tokens, partition_size, cpu
     inp, q, qs, max_q = prefill_inputs(new_tokens=[new_tokens] * batch, seed=77, device=dev,
                                        num_seqs=batch, num_heads=64, num_kv_heads=8,
                                        head_size=128, block_size=16, dtype="bf16",
-                                       context_lens=context)
+                                       context_lens=context, kv_dtype=kv_dtype)
     out = torch.empty_like(q)
 
     def step():
         paged_attention_prefill(out, q, inp.key_cache, inp.value_cache, inp.block_tables,
                                 inp.context_lens, qs, max_q, inp.scale, 16,
-                                partition_size=partition_size)
+                                partition_size=partition_size, k_scale=inp.k_scale,
+                                v_scale=inp.v_scale)
 
     for _ in range(warmup):
         step()
@@ -222,10 +225,11 @@ def bench_prefill(steps, warmup, batch, context, new_tokens, partition_size, cpu
     keys = sum(context - new_tokens + i + 1 for i in range(new_tokens)) * batch
     flops = 4 * 64 * 128 * keys
     print(json.dumps({"op": "prefill", "batch": batch, "context": context,
-                      "new_tokens": new_tokens, "us_per_call": round(sec * 1e6, 2),
+                      "new_tokens": new_tokens, "kv_cache": kv_dtype or "bf16",
+                      "us_per_call": round(sec * 1e6, 2),
                       "TFLOP/s": round(flops / sec / 1e12, 2),
                       "pct_of_mfma_peak": round(100 * flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
-                      **({"cpu_baseline": cpu_baseline_prefill(context, new_tokens, cpu_seconds)}
+                      **({"cpu_baseline": cpu_baseline_prefill(context, new_tokens, cpu_seconds, kv_dtype)}
                          if cpu_seconds > 0 else {})}),
           flush=True)
 
@@ -343,7 +347,7 @@ def main():
         return
     if a.op == "prefill":
         bench_prefill(a.steps, a.warmup, a.batch or 4, a.context, a.new_tokens, a.partition_size,
-                      0.0 if a.no_cpu_baseline else min(a.cpu_seconds, 5.0))
+                      0.0 if a.no_cpu_baseline else min(a.cpu_seconds, 5.0), a.kv_dtype)
         return
     if a.op != "decode":
         bench_copy(a.op, a.steps, a.warmup, a.tokens, 0.0 if a.no_cpu_baseline else min(a.cpu_seconds, 3.0))
