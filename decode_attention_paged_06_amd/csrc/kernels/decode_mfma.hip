@@ -12,8 +12,8 @@
 //   S^T[t, g]   = sum_d K[t, d] q[g, d]    v_mfma_f32_16x16x32_{f16,bf16}, D/32 steps
 //   O^T[d, g]  += sum_t V[t, d] P[g, t]     v_mfma_f32_16x16x16_{f16,bf16}, D/16 tiles
 //
-// (multi-query calls take key tiles in pairs, KT = 2, and run P.V on the
-// 16x16x32 form over the pair's 32 keys).
+// (multi-query calls, and staged decode over FP8 caches, take key tiles in
+// pairs, KT = 2, and run P.V on the 16x16x32 form over the pair's 32 keys).
 //
 // The workgroup has NT x TG waves: wave w computes head tile w % NT (RT
 // consecutive 16-row tiles of query rows for multi-query calls, which share
@@ -148,7 +148,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   constexpr bool STAGE = NT > 1;
   // KT = 2: the LDS ring holds pairs of consecutive tiles, processed together
   // (one softmax max per 32 keys; P.V on the 32-deep MFMA, whose two operands
-  // are the two tiles' 16-key operands side by side)
+  // are the two tiles' 16-key operands side by side); multi-query calls and
+  // staged decode over FP8 caches
   static_assert(KT == 1 || (KT == 2 && STAGE), "tile pairs are staged");
   constexpr int kRing = KT == 2 ? 3 : 4;  // ring slots (of KT tiles)
   // A staged tile: K as per-lane 16-byte pieces, V as the tile's own 16 rows
@@ -641,7 +642,11 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
 // through the LDS ring) take 4 token groups, 12 waves (measured against 2:
 // MQA ragged batch 256 148 -> 134 us; against 3: 133 -> 126 us).  For one
 // head tile, 1-3 token groups were measured slower or, with one group, unfit
-// for ragged batches (a whole sequence on one wave).
+// for ragged batches (a whole sequence on one wave).  With an FP8 cache the
+// staged decode takes tile pairs (half-size slots; the per-key softmax and
+// step overhead, not the bytes, bound it: MQA 124.5 -> 113 us, 64-head groups
+// 142 -> 128 us); 16-bit caches keep single tiles (pairs fit only a 2-slot
+// ring for 4 token groups: MQA 122 -> 135 us).
 template <typename Fmt, int D, bool KV8>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   // multi-query: kPrefillWaves waves of kPrefillRowTilesPerWave 16-row tiles
@@ -650,9 +655,9 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
     return launch_t<Fmt, D, kPrefillWaves, 1, kPrefillRowTilesPerWave, 2, KV8>(a, s);
   switch (mfma_head_tiles(a.group)) {
     case 1: return launch_t<Fmt, D, 1, 4, 1, 1, KV8>(a, s);
-    case 2: return launch_t<Fmt, D, 2, 2, 1, 1, KV8>(a, s);
-    case 3: return launch_t<Fmt, D, 3, 4, 1, 1, KV8>(a, s);
-    default: return launch_t<Fmt, D, 4, 1, 1, 1, KV8>(a, s);
+    case 2: return launch_t<Fmt, D, 2, 2, 1, KV8 ? 2 : 1, KV8>(a, s);
+    case 3: return launch_t<Fmt, D, 3, 4, 1, KV8 ? 2 : 1, KV8>(a, s);
+    default: return launch_t<Fmt, D, 4, 1, 1, KV8 ? 2 : 1, KV8>(a, s);
   }
 }
 
