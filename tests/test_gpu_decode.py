@@ -264,6 +264,19 @@ def test_fp8_workload_full_size():
         compare(run(inp, engine=engine), ref, "bf16", seqs, what=f"fp8 gqa4096 b64 {engine}")
 
 
+def test_fp8_mqa_workload_full_size():
+    """The MQA 48/1 ragged ALiBi batch-256 workload with an fp8 cache (the staged
+    path on tile pairs, split, longest first), sampled against the oracle."""
+    dev = device()
+    args = workload_args("mqa_ragged_alibi", 256)
+    inp = make(device_=dev, poison=True, kv_dtype="fp8", **args)
+    seqs = sample_seqs(256, 12, seed=4)
+    ref = oracle_ref(inp, seqs)
+    for schedule in ("auto", "grid"):
+        compare(run(inp, schedule=schedule), ref, args["dtype"], seqs,
+                what=f"fp8 mqa ragged b256 {schedule}")
+
+
 # ---------------------------------------------------------------------------
 # Groups of more than 16 heads: the head-tile waves of a token group share
 # each K/V tile through an LDS ring and read block ids from an LDS window of
