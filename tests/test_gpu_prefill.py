@@ -96,3 +96,27 @@ def test_prefill_table_window():
     ref = ref_prefill(inp, q, qs)
     for ps in (-1, 0, 4096):
         compare(run_prefill(inp, q, qs, max_q, ps), ref, "f16", what=f"window partition={ps}")
+
+
+@pytest.mark.parametrize("kv", [None, "fp8"])
+def test_prefill_bench_shape_sampled(kv):
+    """The multi-query shape bench.py times (GQA 64/8 bf16, 4 sequences x 512 new
+    tokens on 4096 context, automatic plan), checked on sampled rows: a new token's
+    rows equal decode of that token over the context cut at its position (an
+    identity the oracle's own pins check), so the fp64 decode oracle serves."""
+    dev = device()
+    S, L, n = 4, 4096, 512
+    inp, q, qs, max_q = prefill_inputs(new_tokens=[n] * S, seed=77, device=dev, num_seqs=S,
+                                       num_heads=64, num_kv_heads=8, head_size=128,
+                                       block_size=16, dtype="bf16", context_lens=L, kv_dtype=kv)
+    out = run_prefill(inp, q, qs, max_q)
+    rng = np.random.default_rng(5)
+    picks = [(s, i) for s in range(S) for i in (0, n - 1, int(rng.integers(1, n - 1)))]
+    starts = qs.cpu().numpy()
+    rows = [int(starts[s]) + i for s, i in picks]
+    tables = inp.block_tables.cpu().numpy()[[s for s, _ in picks]]
+    lens = np.array([L - n + i + 1 for _, i in picks], dtype=np.int64)
+    ref = oracle.paged_decode(raw_u16(q[rows]), raw_bits(inp.key_cache), raw_bits(inp.value_cache),
+                              tables, lens, inp.scale, inp.block_size, None, dtype="bf16",
+                              k_scale=inp.k_scale, v_scale=inp.v_scale)
+    compare(out[rows], ref, "bf16", what=f"prefill bench shape ({kv or 'bf16'} cache), sampled rows")
