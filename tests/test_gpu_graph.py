@@ -1,0 +1,88 @@
+"""Decode and multi-query calls captured into a HIP graph and replayed.
+
+A serving loop captures the attention call once and replays it every step.
+The captured work must allocate nothing and record no memory fills, and each
+replay must give exactly what an eager call gives on the same inputs (the
+kernels are deterministic).  Between replays the test writes new query values
+with ordinary eager work and synchronises, as a decode loop would.
+"""
+import pytest
+import torch
+
+from decode_attention_paged_06_amd import paged_attention_decode, paged_attention_prefill
+from gpu_util import device, make, to_device
+from workloads import prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+WS_BYTES = 64 << 20
+
+DECODE_CASES = {
+    # small batch, long context: split partitions + reduce
+    "gqa_split": dict(num_seqs=2, num_heads=64, num_kv_heads=8, head_size=128, block_size=16,
+                      dtype="bf16", context_lens=3000),
+    # 48-head groups, ragged, ALiBi: unit-order kernel + staged decode + reduce
+    "mqa_longest_first": dict(num_seqs=32, num_heads=48, num_kv_heads=1, head_size=128,
+                              block_size=16, dtype="f16", context_lens=(64, 4000), alibi=True),
+    # FP8 cache, one pass
+    "gqa_fp8_single": dict(num_seqs=64, num_heads=64, num_kv_heads=8, head_size=128,
+                           block_size=16, dtype="bf16", context_lens=700, kv_dtype="fp8"),
+    # MHA on the VALU engine
+    "mha_valu": dict(num_seqs=8, num_heads=40, num_kv_heads=40, head_size=128, block_size=16,
+                     dtype="f16", context_lens=256),
+}
+
+
+def capture_and_check(call, query, what):
+    dev = query.device
+    ws_g = torch.empty(WS_BYTES, dtype=torch.uint8, device=dev)
+    ws_e = torch.empty(WS_BYTES, dtype=torch.uint8, device=dev)
+    out_g = torch.full_like(query, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out_g, ws_g)  # first call outside the capture (device attributes are cached)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out_g, ws_g)
+    gen = torch.Generator(device=dev).manual_seed(11)
+    for rep in range(4):
+        query.copy_(torch.randn(query.shape, generator=gen, device=dev).to(query.dtype))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        out_e = torch.full_like(query, float("nan"))
+        call(out_e, ws_e)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out_g.float()).all(), f"{what} replay {rep}: non-finite output"
+        assert torch.equal(out_g, out_e), f"{what} replay {rep}: differs from the eager call"
+
+
+@pytest.mark.parametrize("case", list(DECODE_CASES))
+def test_decode_graph_replay(case):
+    dev = device()
+    inp = to_device(make(seed=31, poison=True, **DECODE_CASES[case]), dev)
+
+    def call(out, ws):
+        paged_attention_decode(out, inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
+                               inp.context_lens, inp.scale, inp.block_size, inp.alibi_slopes,
+                               workspace=ws, k_scale=inp.k_scale, v_scale=inp.v_scale)
+
+    capture_and_check(call, inp.query, case)
+
+
+def test_prefill_graph_replay():
+    dev = device()
+    inp, q, qs, max_q = prefill_inputs(new_tokens=[40, 1, 300, 7], seed=32, device=dev,
+                                       num_seqs=4, num_heads=32, num_kv_heads=4, head_size=128,
+                                       block_size=16, dtype="bf16",
+                                       context_lens=[100, 2000, 900, 7], alibi=True, poison=True)
+
+    def call(out, ws):
+        paged_attention_prefill(out, q, inp.key_cache, inp.value_cache, inp.block_tables,
+                                inp.context_lens, qs, max_q, inp.scale, inp.block_size,
+                                inp.alibi_slopes, workspace=ws, partition_size=256)
+
+    capture_and_check(call, q, "prefill")
