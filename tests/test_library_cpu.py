@@ -301,3 +301,33 @@ def test_status_strings(L):
     for code in range(7):
         assert L.pa_status_string(code).decode()
     assert L.pa_status_string(99).decode() == "unknown status"
+
+
+def test_last_error_is_per_thread(L):
+    """Concurrent callers each read their own failure message (the foreign calls
+    release the interpreter lock, so the threads do run in the library at once)."""
+    import threading
+
+    L.pa_last_error.restype = ctypes.c_char_p
+    failures = []
+
+    def worker(t):
+        bad = dims(Hq=64 + t, Hkv=8)  # not a multiple: the message names 64 + t
+        good = dims(S=256)
+        for _ in range(2000):
+            st, _ = plan(L, bad)
+            msg = L.pa_last_error().decode()
+            if st != INVALID or f"({64 + t})" not in msg:
+                failures.append((t, st, msg))
+                return
+            st, _ = plan(L, good)
+            if st != OK or L.pa_last_error().decode() != "":
+                failures.append((t, st, "not cleared"))
+                return
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(1, 7)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not failures, failures[:3]
