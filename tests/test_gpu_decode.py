@@ -217,6 +217,30 @@ def test_stream_argument_is_used():
     compare(out, ref, "bf16", what="side stream")
 
 
+def test_concurrent_streams():
+    """Calls in flight on two streams at once, each with its own workspace (a
+    split GQA call and a longest-first MQA call), give what each gives alone."""
+    dev = device()
+    a = to_device(make(num_seqs=3, num_heads=64, num_kv_heads=8, head_size=128, block_size=16,
+                       dtype="bf16", seed=43, context_lens=[2500, 40, 4000]), dev)
+    b = to_device(make(num_seqs=24, num_heads=48, num_kv_heads=1, head_size=128, block_size=16,
+                       dtype="f16", seed=44, context_lens=(64, 3000), alibi=True), dev)
+    want = [run(a), run(b)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    ws = [torch.empty(32 << 20, dtype=torch.uint8, device=dev) for _ in range(2)]
+    outs = [torch.full_like(x.query, float("nan")) for x in (a, b)]
+    from decode_attention_paged_06_amd import paged_attention_decode
+    for _ in range(10):
+        for k, inp in enumerate((a, b)):
+            with torch.cuda.stream(streams[k]):
+                paged_attention_decode(outs[k], inp.query, inp.key_cache, inp.value_cache,
+                                       inp.block_tables, inp.context_lens, inp.scale, 16,
+                                       inp.alibi_slopes, stream=streams[k], workspace=ws[k])
+    torch.cuda.synchronize()
+    for k in range(2):
+        assert torch.equal(outs[k], want[k]), f"stream {k} differs from its call alone"
+
+
 # ---------------------------------------------------------------------------
 # FP8 E4M3 caches (one scale per cache tensor)
 # ---------------------------------------------------------------------------
