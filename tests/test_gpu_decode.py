@@ -363,3 +363,32 @@ def test_reduce_partition_counts(engine):
     for ps in (16, 32, 64, 128, 256, 1024):  # up to 138 partitions of the longest sequence
         compare(run(inp, engine=engine, partition_size=ps), ref, "bf16",
                 what=f"{engine} partition={ps}")
+
+
+# ---------------------------------------------------------------------------
+# Maximum sizes: the largest batch the ABI takes (65535 sequences, the grid's
+# y limit; split and longest-first grids of ~200k units) and a 65536-token
+# context (hundreds of partitions into one reduce).
+# ---------------------------------------------------------------------------
+
+def test_maximum_batch():
+    dev = device()
+    S = 65535
+    inp = to_device(make(num_seqs=S, num_heads=16, num_kv_heads=2, head_size=64, block_size=16,
+                         dtype="bf16", seed=51, context_lens=(1, 40)), dev)
+    seqs = sample_seqs(S, 12, seed=5)
+    ref = oracle_ref(inp, seqs)
+    compare(run(inp), ref, "bf16", seqs, what="65535 sequences, one pass")
+    compare(run(inp, partition_size=16), ref, "bf16", seqs, what="65535 sequences, split")
+    compare(run(inp, partition_size=16, schedule="longest_first"), ref, "bf16", seqs,
+            what="65535 sequences, split, longest first")
+
+
+@pytest.mark.parametrize("block_size", [16, 256])
+def test_maximum_context(block_size):
+    dev = device()
+    inp = to_device(make(num_seqs=1, num_heads=64, num_kv_heads=1, head_size=128,
+                         block_size=block_size, dtype="bf16", seed=52, context_lens=65536,
+                         alibi=True, poison=True), dev)
+    ref = oracle_ref(inp)
+    compare(run(inp), ref, "bf16", what=f"65536-token context, block {block_size}, auto plan")
