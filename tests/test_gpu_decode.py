@@ -392,3 +392,20 @@ def test_maximum_context(block_size):
                          alibi=True, poison=True), dev)
     ref = oracle_ref(inp)
     compare(run(inp), ref, "bf16", what=f"65536-token context, block {block_size}, auto plan")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_large_logits(engine, dtype):
+    """q and K scaled by 16: logits in the thousands, a nearly one-hot softmax;
+    the running max and rescale keep every weight finite, split or not."""
+    dev = device()
+    inp = to_device(make(num_seqs=4, num_heads=16, num_kv_heads=2, head_size=128, block_size=16,
+                         dtype=dtype, seed=53, context_lens=[1, 300, 1000, 2500], alibi=True,
+                         poison=True), dev)
+    inp.query.mul_(16)
+    inp.key_cache.mul_(16)
+    ref = oracle_ref(inp)
+    for ps in (-1, 128):
+        compare(run(inp, engine=engine, partition_size=ps), ref, dtype,
+                what=f"large logits {dtype} {engine} partition={ps}")
