@@ -591,13 +591,15 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   }
 
   // ---- finalise ---------------------------------------------------------------
+  // A row whose visible keys (0 .. pos) all lie in partition 0 is finished
+  // here; the reduce skips it.
   if (tg != 0) return;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     if (!row_ok[rt]) continue;
     const float inv = lsum[rt] > 0.f ? a.v_scale / lsum[rt] : 0.f;
     const size_t orow_idx = (size_t)(q_first + ti[rt]) * a.num_heads + h0 + g[rt];
-    if (single) {
+    if (single || (part == 0 && pos[rt] < a.partition_blocks * BS)) {
       uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + orow_idx * D;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {

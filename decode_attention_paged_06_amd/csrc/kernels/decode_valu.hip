@@ -264,13 +264,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
   }
 
   // ---- finalise -------------------------------------------------------------
+  // A sequence whose keys all lie in partition 0 is finished here; the reduce
+  // skips it.
+  const bool direct = single || (part == 0 && L <= a.partition_blocks * BS);
   if (wave != 0 || rho != 0) return;
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
     if (g >= nh) break;
     const float inv = l[g] > 0.f ? a.v_scale / l[g] : 0.f;
     const size_t row = (size_t)seq * a.num_heads + h0 + g;
-    if (single) {
+    if (direct) {
       uint4 o;
       o.x = Fmt::pack(acc[g][0] * inv, acc[g][1] * inv);
       o.y = Fmt::pack(acc[g][2] * inv, acc[g][3] * inv);

@@ -11,7 +11,9 @@
 //   M = max_p m_p,  w_p = l_p * exp2(m_p - M),  out = sum_p w_p o_p / sum_p w_p
 // over the partitions that hold keys the row sees (p < ceil(visible /
 // partition_size), visible = L_s for decode, position + 1 for a new token of a
-// multi-query call).  One wave per (head, sequence, new token).  The (m_p,
+// multi-query call).  A row with a single such partition was written by the
+// decode kernel itself and is skipped here.  One wave per (head, sequence, new
+// token).  The (m_p,
 // l_p) pairs are read one partition per lane (64 at a time) and reduced across
 // the wave; the partial outputs are read in batches whose loads are all in
 // flight together, so a row costs a few memory round trips however many
@@ -112,6 +114,7 @@ __global__ __launch_bounds__(64) void partition_reduce_kernel(const DecodeArgs a
   const int ptok = a.partition_blocks * a.block_size;
   const int visible = L - n_new + i + 1;
   const int nact = min(a.num_partitions, (visible + ptok - 1) / ptok);
+  if (nact == 1) return;  // the decode kernel wrote this row (all its keys in partition 0)
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + row * a.num_partitions;
   const Part* o = reinterpret_cast<const Part*>(a.ws_o + row * a.num_partitions * D) + lane;
 
