@@ -11,6 +11,10 @@ algorithmic bytes are K and V of every context token once per kv head, q in,
 out back, one block-table entry per used block and the context lengths
 (plus the slopes with ALiBi).
 
+The caches are laid out joint by default (one [NB, Hkv, 2, BS, D] tensor: the
+K and V tiles of each block and kv head side by side); --kv-layout separate
+times two [NB, Hkv, BS, D] tensors.  Results are identical either way.
+
 Caches are defeated by rotating over independent input sets whose combined
 footprint is at least 2 GiB (the headline workload alone is 4.3 GB, so it
 uses a single set).
@@ -48,6 +52,9 @@ def parse():
                     help="order of the work units of a split plan (see pa_schedule)")
     ap.add_argument("--kv-dtype", default=None, choices=["fp8"],
                     help="store the K/V caches as FP8 E4M3 (scale 1/16) instead of the query type")
+    ap.add_argument("--kv-layout", default="joint", choices=["joint", "separate"],
+                    help="cache layout: one [NB, Hkv, 2, BS, D] tensor (K and V tiles of each "
+                         "block and kv head side by side) or two [NB, Hkv, BS, D] tensors")
     ap.add_argument("--block-size", type=int, default=0,
                     help="override the workload's cache block size (tokens per block)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -103,7 +110,7 @@ def cpu_baseline_copy(op, num_tokens, budget_s):
             "sample": f"{calls} full calls at the same shapes ({dt * 1e3:.1f} ms each, numpy)"}
 
 
-def bench_copy(op, steps, warmup, num_tokens, cpu_seconds=0.0):
+def bench_copy(op, steps, warmup, num_tokens, cpu_seconds=0.0, kv_layout="separate"):
     """Time gather_cached_kv or paged_kv_cache_write at the gather page's shapes."""
     import torch
 
@@ -116,7 +123,7 @@ def bench_copy(op, steps, warmup, num_tokens, cpu_seconds=0.0):
     # rotate pools so the ~2 GiB working set defeats the 256 MB last-level cache
     for i in range(max(1, -(-ROTATE_BYTES // (2 * NB * H * BS * D * 2)))):
         g = gather_inputs(num_tokens=num_tokens, num_kv_heads=H, head_size=D, block_size=BS,
-                          num_blocks=NB, dtype="f16", seed=29 + i, device=dev)
+                          num_blocks=NB, dtype="f16", seed=29 + i, device=dev, kv_layout=kv_layout)
         rows = (torch.empty((num_tokens, H, D), dtype=torch.float16, device=dev),
                 torch.empty((num_tokens, H, D), dtype=torch.float16, device=dev))
         sets.append((g, rows))
@@ -150,7 +157,8 @@ def bench_copy(op, steps, warmup, num_tokens, cpu_seconds=0.0):
     once = copy_bytes_once(num_tokens, H, D, 2)
     moved = 2 * once + 4 * num_tokens  # read and write every row, plus the slots
     print(json.dumps({"op": op, "num_tokens": num_tokens, "num_kv_heads": H, "head_size": D,
-                      "block_size": BS, "num_blocks": NB, "dtype": "f16", "us_per_call": round(sec * 1e6, 3),
+                      "block_size": BS, "num_blocks": NB, "dtype": "f16", "kv_layout": kv_layout,
+                      "us_per_call": round(sec * 1e6, 3),
                       "GB/s_read_plus_write": round(moved / sec / 1e9, 2),
                       "pct_of_hbm_peak": round(100 * moved / sec / 1e9 / HBM_PEAK_GBPS, 2),
                       "pages_convention_GiB/s": round(pages_gib_per_s(num_tokens, H, D, 2, sec), 2),
@@ -189,7 +197,7 @@ def cpu_baseline_prefill(context, new_tokens, budget_s, kv_dtype=None):
 
 
 def bench_prefill(steps, warmup, batch, context, new_tokens, partition_size, cpu_seconds=0.0,
-                  kv_dtype=None):
+                  kv_dtype=None, kv_layout="separate"):
     """Time causal multi-query attention: `new_tokens` queries per sequence over a
     `context`-token paged cache (GQA 64/8, D 128, bf16, block 16; FP8 E4M3 cache
     with kv_dtype="fp8")."""
@@ -202,7 +210,8 @@ def bench_prefill(steps, warmup, batch, context, new_tokens, partition_size, cpu
     inp, q, qs, max_q = prefill_inputs(new_tokens=[new_tokens] * batch, seed=77, device=dev,
                                        num_seqs=batch, num_heads=64, num_kv_heads=8,
                                        head_size=128, block_size=16, dtype="bf16",
-                                       context_lens=context, kv_dtype=kv_dtype)
+                                       context_lens=context, kv_dtype=kv_dtype,
+                                       kv_layout=kv_layout)
     out = torch.empty_like(q)
 
     def step():
@@ -225,7 +234,7 @@ def bench_prefill(steps, warmup, batch, context, new_tokens, partition_size, cpu
     keys = sum(context - new_tokens + i + 1 for i in range(new_tokens)) * batch
     flops = 4 * 64 * 128 * keys
     print(json.dumps({"op": "prefill", "batch": batch, "context": context,
-                      "new_tokens": new_tokens, "kv_cache": kv_dtype or "bf16",
+                      "new_tokens": new_tokens, "kv_cache": kv_dtype or "bf16", "kv_layout": kv_layout,
                       "us_per_call": round(sec * 1e6, 2),
                       "TFLOP/s": round(flops / sec / 1e12, 2),
                       "pct_of_mfma_peak": round(100 * flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
@@ -251,15 +260,15 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 def recorded_traffic(kernel: str, workload: str, batch: int, kv: str = "native",
-                     block_size: int = 16):
+                     block_size: int = 16, kv_layout: str = "separate"):
     """HBM bytes per launch from a committed rocprofv3 PMC summary, or None.
 
     A summary under profiles/ ends with a JSON record of the scaled
     FETCH_SIZE + WRITE_SIZE traffic and a SHA-256 of the kernel's sources at
     the time the counters were taken; the figure is used only for the same
-    workload, batch, cache format and block size (a record without the last
-    two is of a 16-bit cache with 16-token blocks), and only while the sources
-    still hash the same.
+    workload, batch, cache format, block size and cache layout (a record
+    without the last three is of a 16-bit cache with 16-token blocks in two
+    separate tensors), and only while the sources still hash the same.
     """
     import glob
     import hashlib
@@ -272,7 +281,8 @@ def recorded_traffic(kernel: str, workload: str, batch: int, kv: str = "native",
             rec = json.loads(line)
             if (kernel not in rec["kernel"] or rec["workload"] != workload
                     or rec["batch"] != batch or rec.get("kv", "native") != kv
-                    or rec.get("block_size", 16) != block_size):
+                    or rec.get("block_size", 16) != block_size
+                    or rec.get("kv_layout", "separate") != kv_layout):
                 continue
             h = hashlib.sha256()
             try:
@@ -311,6 +321,7 @@ def cpu_baseline(args, budget_s):
     sample_args = dict(args)
     n = min(args["num_seqs"], 64)
     sample_args["num_seqs"] = n
+    sample_args.pop("kv_layout", None)   # the oracle reads plain [NB, Hkv, BS, D] arrays
     inp = decode_inputs(device="cpu", **sample_args)
     q, kc, vc = raw_u16(inp.query), raw_u16(inp.key_cache), raw_u16(inp.value_cache)
     tables, lens = inp.block_tables.numpy(), inp.context_lens.numpy()
@@ -347,16 +358,18 @@ def main():
         return
     if a.op == "prefill":
         bench_prefill(a.steps, a.warmup, a.batch or 4, a.context, a.new_tokens, a.partition_size,
-                      0.0 if a.no_cpu_baseline else min(a.cpu_seconds, 5.0), a.kv_dtype)
+                      0.0 if a.no_cpu_baseline else min(a.cpu_seconds, 5.0), a.kv_dtype,
+                      a.kv_layout)
         return
     if a.op != "decode":
-        bench_copy(a.op, a.steps, a.warmup, a.tokens, 0.0 if a.no_cpu_baseline else min(a.cpu_seconds, 3.0))
+        bench_copy(a.op, a.steps, a.warmup, a.tokens, 0.0 if a.no_cpu_baseline else min(a.cpu_seconds, 3.0),
+                   a.kv_layout)
         return
 
     import torch
 
-    from decode_attention_paged_06_amd import (make_dims, make_opts, paged_attention_decode,
-                                               paged_attention_plan)
+    from decode_attention_paged_06_amd import (kv_layout_of, make_dims, make_opts,
+                                               paged_attention_decode, paged_attention_plan)
     from workloads import HEADLINE, algorithmic_bytes, algorithmic_flops, decode_inputs, workload_args
 
     name = a.workload or HEADLINE[0]
@@ -364,6 +377,7 @@ def main():
     args = workload_args(name, batch)
     if a.kv_dtype:
         args["kv_dtype"] = a.kv_dtype
+    args["kv_layout"] = a.kv_layout
     if a.block_size:
         args["block_size"] = a.block_size
         args.pop("pool_blocks", None)  # pool sized to fit the new block size
@@ -390,7 +404,7 @@ def main():
     outs = [torch.empty_like(s.query) for s in sets]
 
     dims = make_dims(first.query, first.key_cache, first.block_tables, first.k_scale,
-                     first.v_scale)
+                     first.v_scale, kv_layout_of(first.key_cache, first.value_cache))
     opts = make_opts(a.partition_size, a.engine, schedule=a.schedule)
     plan = paged_attention_plan(dims, 1 << 40, opts)
     workspace = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
@@ -482,7 +496,7 @@ def main():
             "workload": workload_label(name, args),
             "num_seqs": batch, "num_heads": args["num_heads"], "num_kv_heads": args["num_kv_heads"],
             "head_size": args["head_size"], "block_size": args["block_size"],
-            "kv_cache": args.get("kv_dtype") or args["dtype"],
+            "kv_cache": args.get("kv_dtype") or args["dtype"], "kv_layout": a.kv_layout,
             "context_lens": str(args["context_lens"]), "seed": args["seed"],
             "engine": {0: "auto", 1: "valu", 2: "mfma"}[plan.engine] if a.engine == "auto" else a.engine,
             "num_partitions": plan.num_partitions, "partition_size": plan.partition_size,
@@ -499,7 +513,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": recorded_traffic(kernel_name, name, batch, a.kv_dtype or "native",
-                                        args["block_size"]),
+                                        args["block_size"], a.kv_layout),
             "kernel": kernel_name,
             "kernel_avg_us": round(avg_ms * 1e3, 2),
             "flops_per_call": flops,

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "libpagedattn.so")
 
 PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_KV_NATIVE, PA_KV_FP8_E4M3 = 0, 1
+PA_KV_SEPARATE, PA_KV_JOINT = 0, 1
 PA_ENGINE_AUTO, PA_ENGINE_VALU, PA_ENGINE_MFMA = 0, 1, 2
 PA_SCHEDULE_AUTO, PA_SCHEDULE_GRID, PA_SCHEDULE_LONGEST_FIRST = 0, 1, 2
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_ALIGNMENT",
@@ -31,7 +32,7 @@ class PaDims(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("kv_format", ctypes.c_int32), ("k_scale", ctypes.c_float),
-                ("v_scale", ctypes.c_float)]
+                ("v_scale", ctypes.c_float), ("kv_layout", ctypes.c_int32)]
 
 
 class PaOpts(ctypes.Structure):
@@ -81,9 +82,9 @@ def lib() -> ctypes.CDLL:
     L.paged_attention_prefill_plan.argtypes = [ctypes.POINTER(PaDims), i32, i32, sz,
                                                ctypes.POINTER(PaOpts), ctypes.POINTER(PaPlan)]
     L.paged_attention_prefill_plan.restype = ctypes.c_int
-    L.gather_cached_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.gather_cached_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     L.gather_cached_kv.restype = ctypes.c_int
-    L.paged_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.paged_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     L.paged_kv_cache_write.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p

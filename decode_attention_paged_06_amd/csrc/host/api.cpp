@@ -82,6 +82,8 @@ int check_dims(const pa_dims* d) {
     return fail(PA_ERR_INVALID_ARG, "context bound max_blocks_per_seq * block_size too large");
   if (d->kv_format != PA_KV_NATIVE && d->kv_format != PA_KV_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "kv_format %d", d->kv_format);
+  if (d->kv_layout != PA_KV_SEPARATE && d->kv_layout != PA_KV_JOINT)
+    return fail(PA_ERR_INVALID_ARG, "kv_layout %d", d->kv_layout);
   if (d->kv_format == PA_KV_FP8_E4M3) {
     const float inf = __builtin_inff();
     if (!(d->k_scale > 0.f) || !(d->v_scale > 0.f) || d->k_scale == inf || d->v_scale == inf)
@@ -91,6 +93,26 @@ int check_dims(const pa_dims* d) {
 }
 
 size_t elem_bytes(int32_t dtype) { return dtype == PA_FP8_E4M3 ? 1 : 2; }
+
+// Byte strides of the caches' (block, kv head) tiles for a pa_kv_layout, and
+// the joint layout's pointer relation (value tiles follow key tiles).
+int cache_strides(int32_t layout, int32_t num_kv_heads, int32_t block_size, size_t row_bytes,
+                  const void* key_cache, const void* value_cache, int64_t* block_stride,
+                  int64_t* head_stride) {
+  const int64_t tile = (int64_t)block_size * (int64_t)row_bytes;
+  if (layout == PA_KV_SEPARATE) {
+    *head_stride = tile;
+    *block_stride = tile * num_kv_heads;
+    return PA_OK;
+  }
+  if (layout != PA_KV_JOINT) return fail(PA_ERR_INVALID_ARG, "kv_layout %d", layout);
+  if (static_cast<const char*>(value_cache) != static_cast<const char*>(key_cache) + tile)
+    return fail(PA_ERR_INVALID_ARG,
+                "joint K/V layout: value_cache must be key_cache + block_size * head_size elements");
+  *head_stride = 2 * tile;
+  *block_stride = 2 * tile * num_kv_heads;
+  return PA_OK;
+}
 
 int current_num_cus(int* out) {
   int dev = 0;
@@ -272,6 +294,13 @@ int run_attention(void* out, const void* query, const void* key_cache, const voi
     return fail(PA_ERR_ALIGNMENT,
                 "block_tables, context_lens, query_start_loc and alibi_slopes must be 4-byte aligned");
 
+  const bool kv_fp8 = dims->kv_format == PA_KV_FP8_E4M3;
+  int64_t kv_block_stride = 0, kv_head_stride = 0;
+  if ((st = cache_strides(dims->kv_layout, dims->num_kv_heads, dims->block_size,
+                          (size_t)dims->head_size * (kv_fp8 ? 1 : 2), key_cache, value_cache,
+                          &kv_block_stride, &kv_head_stride)))
+    return st;
+
   pa_plan plan;
   if ((st = make_plan(dims, c, workspace ? workspace_bytes : 0, opts, false, &plan))) return st;
   if (plan.num_partitions > 1) {
@@ -288,7 +317,8 @@ int run_attention(void* out, const void* query, const void* key_cache, const voi
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.alibi = alibi_slopes;
-  const bool kv_fp8 = dims->kv_format == PA_KV_FP8_E4M3;
+  a.kv_block_stride = kv_block_stride;
+  a.kv_head_stride = kv_head_stride;
   // the key scale folds into the logit scale, the value scale into the output
   a.scale_log2 = scale * 1.4426950408889634f * (kv_fp8 ? dims->k_scale : 1.f);
   a.v_scale = kv_fp8 ? dims->v_scale : 1.f;
@@ -449,18 +479,25 @@ static int check_copy_args(int32_t num_tokens, int32_t num_kv_heads, int32_t hea
 int paged_kv_cache_write(void* key_cache, void* value_cache, const void* key, const void* value,
                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                          int32_t head_size, int32_t block_size, int32_t num_blocks, int32_t dtype,
-                         pa_stream_t stream) {
+                         int32_t kv_layout, pa_stream_t stream) {
   int st = check_copy_args(num_tokens, num_kv_heads, head_size, block_size, num_blocks, dtype);
   if (st) return st;
+  if (kv_layout != PA_KV_SEPARATE && kv_layout != PA_KV_JOINT)
+    return fail(PA_ERR_INVALID_ARG, "kv_layout %d", kv_layout);
   if (num_tokens == 0) return ok();
   if (!key_cache || !value_cache || !key || !value || !slot_mapping)
     return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(key, 16) ||
       !aligned(value, 16) || !aligned(slot_mapping, 4))
     return fail(PA_ERR_ALIGNMENT, "16-bit tensors must be 16-byte aligned, slot_mapping 4-byte");
+  const size_t row_bytes = (size_t)head_size * elem_bytes(dtype);
+  int64_t bstride = 0, hstride = 0;
+  if ((st = cache_strides(kv_layout, num_kv_heads, block_size, row_bytes, key_cache, value_cache,
+                          &bstride, &hstride)))
+    return st;
   const hipError_t e = pa::launch_cache_write(key_cache, value_cache, key, value, slot_mapping,
-                                              num_tokens, num_kv_heads,
-                                              head_size * (int32_t)elem_bytes(dtype), block_size,
+                                              num_tokens, num_kv_heads, (int32_t)row_bytes,
+                                              block_size, bstride, hstride,
                                               reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "cache write launch: %s", hipGetErrorString(e));
   return ok();
@@ -469,19 +506,25 @@ int paged_kv_cache_write(void* key_cache, void* value_cache, const void* key, co
 int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
                      const void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
                      int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                     int32_t num_blocks, int32_t dtype, pa_stream_t stream) {
+                     int32_t num_blocks, int32_t dtype, int32_t kv_layout, pa_stream_t stream) {
   int st = check_copy_args(num_tokens, num_kv_heads, head_size, block_size, num_blocks, dtype);
   if (st) return st;
+  if (kv_layout != PA_KV_SEPARATE && kv_layout != PA_KV_JOINT)
+    return fail(PA_ERR_INVALID_ARG, "kv_layout %d", kv_layout);
   if (num_tokens == 0) return ok();
   if (!key_out || !value_out || !key_cache || !value_cache || !slot_mapping)
     return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(key_out, 16) || !aligned(value_out, 16) || !aligned(key_cache, 16) ||
       !aligned(value_cache, 16) || !aligned(slot_mapping, 4))
     return fail(PA_ERR_ALIGNMENT, "16-bit tensors must be 16-byte aligned, slot_mapping 4-byte");
+  const size_t row_bytes = (size_t)head_size * elem_bytes(dtype);
+  int64_t bstride = 0, hstride = 0;
+  if ((st = cache_strides(kv_layout, num_kv_heads, block_size, row_bytes, key_cache, value_cache,
+                          &bstride, &hstride)))
+    return st;
   const hipError_t e = pa::launch_gather(key_out, value_out, key_cache, value_cache, slot_mapping,
-                                         num_tokens, num_kv_heads,
-                                         head_size * (int32_t)elem_bytes(dtype), block_size,
-                                         reinterpret_cast<hipStream_t>(stream));
+                                         num_tokens, num_kv_heads, (int32_t)row_bytes, block_size,
+                                         bstride, hstride, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "gather launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -300,8 +300,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
 
   // Byte addressing: a wave-uniform tile base (SGPRs) plus a small unsigned
   // per-lane offset, so every K/V load is one buffer load with a VGPR offset.
-  const size_t bstride = (size_t)a.num_kv_heads * BS * D * ES;  // bytes per physical block
-  const size_t head_off = (size_t)kvh * BS * D * ES;
+  const size_t bstride = (size_t)a.kv_block_stride;  // bytes per physical block
+  const size_t head_off = (size_t)kvh * (size_t)a.kv_head_stride;
   const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
   const uint32_t k_lane = (uint32_t)(r * D * ES + j * 16);         // read-0 K chunk

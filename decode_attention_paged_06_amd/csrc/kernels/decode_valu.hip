@@ -100,8 +100,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
   const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
   using KS = KVStore<Fmt, KV8>;  // cache storage: 16-bit, or FP8 converted at use
   constexpr int ES = KS::kBytes;
-  const size_t bstride = (size_t)a.num_kv_heads * BS * D * ES;  // bytes per physical block
-  const size_t head_off = (size_t)kvh * BS * D * ES;
+  const size_t bstride = (size_t)a.kv_block_stride;  // bytes per physical block
+  const size_t head_off = (size_t)kvh * (size_t)a.kv_head_stride;
   const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
   const uint32_t lane_off = (uint32_t)(rho * D + c * 8) * ES;

@@ -6,7 +6,9 @@
 //                        operation that precedes attention in vLLM PR #2744).
 //
 // One thread moves one 16-byte chunk of K and the same chunk of V.  A
-// (token, head) row is head_size * element-size contiguous bytes at both ends, so
+// (token, head) row is head_size * element-size contiguous bytes at both ends
+// (in either cache layout: separate K and V tensors, or K and V tiles of each
+// (block, kv head) side by side), so
 // consecutive threads read and write consecutive 16-byte chunks; a row is
 // never split across a wave boundary for head sizes that divide 64 chunks.
 // Only integer moves: NaN payloads and signed zeros pass through unchanged.
@@ -21,7 +23,8 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(uint4* __restrict__ k_ou
                                                          const uint4* __restrict__ v_cache,
                                                          const int32_t* __restrict__ slots,
                                                          uint32_t total, uint32_t ch,
-                                                         uint32_t hkv, uint32_t bs) {
+                                                         uint32_t hkv, uint32_t bs,
+                                                         uint64_t bstride, uint64_t hstride) {
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
     const uint32_t row = i / ch;          // token * hkv + head
@@ -33,7 +36,7 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(uint4* __restrict__ k_ou
     if (slot >= 0) {
       const uint32_t blk = (uint32_t)slot / bs;
       const uint32_t off = (uint32_t)slot - blk * bs;
-      const size_t src = (((size_t)blk * hkv + head) * bs + off) * ch + c;
+      const size_t src = blk * bstride + head * hstride + (size_t)off * ch + c;
       kv = load_nt(k_cache + src);
       vv = load_nt(v_cache + src);
     }
@@ -48,7 +51,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(uint4* __restrict__ k_
                                                            const uint4* __restrict__ v_new,
                                                            const int32_t* __restrict__ slots,
                                                            uint32_t total, uint32_t ch,
-                                                           uint32_t hkv, uint32_t bs) {
+                                                           uint32_t hkv, uint32_t bs,
+                                                           uint64_t bstride, uint64_t hstride) {
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
     const uint32_t row = i / ch;          // token * hkv + head
@@ -59,7 +63,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(uint4* __restrict__ k_
     if (slot < 0) continue;               // padding token: nothing to store
     const uint32_t blk = (uint32_t)slot / bs;
     const uint32_t off = (uint32_t)slot - blk * bs;
-    const size_t dst = (((size_t)blk * hkv + head) * bs + off) * ch + c;
+    const size_t dst = blk * bstride + head * hstride + (size_t)off * ch + c;
     k_cache[dst] = load_nt(k_new + i);
     v_cache[dst] = load_nt(v_new + i);
   }
@@ -67,7 +71,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(uint4* __restrict__ k_
 
 hipError_t launch_cache_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                               const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                              int32_t row_bytes, int32_t block_size, hipStream_t s) {
+                              int32_t row_bytes, int32_t block_size, int64_t block_stride,
+                              int64_t head_stride, hipStream_t s) {
   const uint32_t ch = (uint32_t)row_bytes / 16;
   const uint32_t total = (uint32_t)num_tokens * (uint32_t)num_kv_heads * ch;
   uint32_t blocks = (total + 255) / 256;
@@ -75,13 +80,14 @@ hipError_t launch_cache_write(void* k_cache, void* v_cache, const void* k_new, c
   cache_write_kernel<<<blocks, 256, 0, s>>>(
       static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), static_cast<const uint4*>(k_new),
       static_cast<const uint4*>(v_new), slots, total, ch, (uint32_t)num_kv_heads,
-      (uint32_t)block_size);
+      (uint32_t)block_size, (uint64_t)block_stride / 16, (uint64_t)head_stride / 16);
   return hipGetLastError();
 }
 
 hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                          const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                         int32_t row_bytes, int32_t block_size, hipStream_t s) {
+                         int32_t row_bytes, int32_t block_size, int64_t block_stride,
+                         int64_t head_stride, hipStream_t s) {
   const uint32_t ch = (uint32_t)row_bytes / 16;
   const uint32_t total = (uint32_t)num_tokens * (uint32_t)num_kv_heads * ch;
   const uint32_t threads = 256;
@@ -90,7 +96,7 @@ hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const vo
   gather_kv_kernel<<<blocks, threads, 0, s>>>(
       static_cast<uint4*>(k_out), static_cast<uint4*>(v_out), static_cast<const uint4*>(k_cache),
       static_cast<const uint4*>(v_cache), slots, total, ch, (uint32_t)num_kv_heads,
-      (uint32_t)block_size);
+      (uint32_t)block_size, (uint64_t)block_stride / 16, (uint64_t)head_stride / 16);
   return hipGetLastError();
 }
 

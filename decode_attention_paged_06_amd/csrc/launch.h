@@ -48,6 +48,10 @@ struct DecodeArgs {
   // (sequence, partition) unit_order[b / (num_kv_heads * row_chunks)], encoded
   // partition * num_seqs + sequence.  nullptr = the grid's own order.
   const int32_t* unit_order = nullptr;
+  // Cache addressing in bytes: the (block, kv head) tile of both caches starts
+  // at block * kv_block_stride + kv_head * kv_head_stride from its base.
+  int64_t kv_block_stride = 0;
+  int64_t kv_head_stride = 0;
 };
 
 // Multi-query workgroups: kPrefillWaves waves, each computing
@@ -81,13 +85,17 @@ hipError_t launch_partition_reduce(const DecodeArgs& a, int dtype, int head_size
 hipError_t launch_unit_order(const DecodeArgs& a, int32_t* order, hipStream_t s);
 
 // Row copies move row_bytes-long rows (a multiple of 16) between the cache and
-// contiguous [num_tokens, num_kv_heads] row arrays.
+// contiguous [num_tokens, num_kv_heads] row arrays.  The cache's (block, kv
+// head) tile starts block * block_stride + kv_head * head_stride bytes from
+// its base (both multiples of 16).
 hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                          const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                         int32_t row_bytes, int32_t block_size, hipStream_t s);
+                         int32_t row_bytes, int32_t block_size, int64_t block_stride,
+                         int64_t head_stride, hipStream_t s);
 
 hipError_t launch_cache_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                               const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                              int32_t row_bytes, int32_t block_size, hipStream_t s);
+                              int32_t row_bytes, int32_t block_size, int64_t block_stride,
+                              int64_t head_stride, hipStream_t s);
 
 }  // namespace pa

@@ -12,7 +12,8 @@ import torch
 
 from . import _lib
 from ._lib import (PA_BF16, PA_ENGINE_AUTO, PA_ENGINE_MFMA, PA_ENGINE_VALU, PA_F16, PA_FP8_E4M3,
-                   PA_KV_FP8_E4M3, PA_KV_NATIVE, PA_SCHEDULE_AUTO, PA_SCHEDULE_GRID,
+                   PA_KV_FP8_E4M3, PA_KV_JOINT, PA_KV_NATIVE, PA_KV_SEPARATE, PA_SCHEDULE_AUTO,
+                   PA_SCHEDULE_GRID,
                    PA_SCHEDULE_LONGEST_FIRST, PaDims, PaOpts, PaPlan, check, lib)
 
 _DTYPE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_FP8_E4M3}
@@ -21,13 +22,43 @@ _SCHEDULE = {"auto": PA_SCHEDULE_AUTO, "grid": PA_SCHEDULE_GRID,
              "longest_first": PA_SCHEDULE_LONGEST_FIRST}
 
 
+def joint_kv_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_size: int,
+                   dtype: torch.dtype, device) -> tuple:
+    """Allocate a cache in the joint layout [NB, Hkv, 2, BS, D] (uninitialised).
+
+    Returns (key_cache, value_cache): views [NB, Hkv, BS, D] of the K and V
+    tiles, which every entry point accepts like two separate tensors.
+    """
+    kv = torch.empty((num_blocks, num_kv_heads, 2, block_size, head_size), dtype=dtype,
+                     device=device)
+    return kv[:, :, 0], kv[:, :, 1]
+
+
+def kv_layout_of(key_cache: torch.Tensor, value_cache: torch.Tensor) -> int:
+    """PA_KV_SEPARATE for two dense caches, PA_KV_JOINT for the two views of
+    one [NB, Hkv, 2, BS, D] tensor; anything else is rejected."""
+    if key_cache.shape != value_cache.shape or key_cache.dim() != 4:
+        raise ValueError("key_cache and value_cache must both be [NB, Hkv, BS, D]")
+    if key_cache.is_contiguous() and value_cache.is_contiguous():
+        return PA_KV_SEPARATE
+    NB, Hkv, BS, D = key_cache.shape
+    joint = (2 * Hkv * BS * D, 2 * BS * D, D, 1)
+    if (key_cache.stride() == joint and value_cache.stride() == joint and
+            value_cache.data_ptr() == key_cache.data_ptr() + BS * D * key_cache.element_size()):
+        return PA_KV_JOINT
+    raise ValueError("caches must be two dense [NB, Hkv, BS, D] tensors or the K and V views "
+                     "of one dense [NB, Hkv, 2, BS, D] tensor")
+
+
 def make_dims(query: torch.Tensor, key_cache: torch.Tensor, block_tables: torch.Tensor,
-              k_scale: float = 1.0, v_scale: float = 1.0) -> PaDims:
+              k_scale: float = 1.0, v_scale: float = 1.0,
+              kv_layout: int = PA_KV_SEPARATE) -> PaDims:
     S, Hq, D = query.shape
     NB, Hkv, BS, D2 = key_cache.shape
     fp8 = key_cache.dtype == torch.float8_e4m3fn
     return PaDims(S, Hq, Hkv, D, BS, NB, block_tables.shape[1], _DTYPE[query.dtype],
-                  PA_KV_FP8_E4M3 if fp8 else PA_KV_NATIVE, float(k_scale), float(v_scale))
+                  PA_KV_FP8_E4M3 if fp8 else PA_KV_NATIVE, float(k_scale), float(v_scale),
+                  int(kv_layout))
 
 
 def make_opts(partition_size: int = 0, engine: str = "auto", num_cus: int = 0,
@@ -41,10 +72,10 @@ def _stream_ptr(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _require(t: torch.Tensor, name: str, dtype=None):
+def _require(t: torch.Tensor, name: str, dtype=None, dense: bool = True):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
+    if dense and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
@@ -78,15 +109,16 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
     _require(out, "out", query.dtype)
     _require(query, "query", query.dtype)
     kv_dtype = torch.float8_e4m3fn if key_cache.dtype == torch.float8_e4m3fn else query.dtype
-    _require(key_cache, "key_cache", kv_dtype)
-    _require(value_cache, "value_cache", kv_dtype)
+    _require(key_cache, "key_cache", kv_dtype, dense=False)
+    _require(value_cache, "value_cache", kv_dtype, dense=False)
+    layout = kv_layout_of(key_cache, value_cache)
     _require(block_tables, "block_tables", torch.int32)
     _require(context_lens, "context_lens", torch.int32)
     if alibi_slopes is not None:
         _require(alibi_slopes, "alibi_slopes", torch.float32)
     if query.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {query.dtype}")
-    dims = make_dims(query, key_cache, block_tables, k_scale, v_scale)
+    dims = make_dims(query, key_cache, block_tables, k_scale, v_scale, layout)
     opts = make_opts(partition_size, engine, schedule=schedule)
     if workspace is None:
         nbytes = paged_attention_workspace_bytes(dims, opts)
@@ -105,8 +137,9 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
 
 
 def make_prefill_dims(query: torch.Tensor, key_cache: torch.Tensor, block_tables: torch.Tensor,
-                      num_seqs: int, k_scale: float = 1.0, v_scale: float = 1.0) -> PaDims:
-    dims = make_dims(query, key_cache, block_tables, k_scale, v_scale)
+                      num_seqs: int, k_scale: float = 1.0, v_scale: float = 1.0,
+                      kv_layout: int = PA_KV_SEPARATE) -> PaDims:
+    dims = make_dims(query, key_cache, block_tables, k_scale, v_scale, kv_layout)
     dims.num_seqs = int(num_seqs)
     return dims
 
@@ -122,8 +155,9 @@ def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: t
     _require(out, "out", query.dtype)
     _require(query, "query", query.dtype)
     kv_dtype = torch.float8_e4m3fn if key_cache.dtype == torch.float8_e4m3fn else query.dtype
-    _require(key_cache, "key_cache", kv_dtype)
-    _require(value_cache, "value_cache", kv_dtype)
+    _require(key_cache, "key_cache", kv_dtype, dense=False)
+    _require(value_cache, "value_cache", kv_dtype, dense=False)
+    layout = kv_layout_of(key_cache, value_cache)
     _require(block_tables, "block_tables", torch.int32)
     _require(context_lens, "context_lens", torch.int32)
     _require(query_start_loc, "query_start_loc", torch.int32)
@@ -131,7 +165,7 @@ def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: t
         _require(alibi_slopes, "alibi_slopes", torch.float32)
     S = context_lens.shape[0]
     T = query.shape[0]
-    dims = make_prefill_dims(query, key_cache, block_tables, S, k_scale, v_scale)
+    dims = make_prefill_dims(query, key_cache, block_tables, S, k_scale, v_scale, layout)
     opts = make_opts(partition_size, "auto")
     if workspace is None:
         nbytes = int(lib().paged_attention_prefill_workspace_bytes(
@@ -155,15 +189,17 @@ def gather_cached_kv(key_out: torch.Tensor, value_out: torch.Tensor, key_cache: 
                      value_cache: torch.Tensor, slot_mapping: torch.Tensor, block_size: int,
                      stream=None):
     """Enqueue the bit-exact gather of cache rows into key_out/value_out ([T, Hkv, D])."""
-    for t, n in ((key_out, "key_out"), (value_out, "value_out"), (key_cache, "key_cache"),
-                 (value_cache, "value_cache")):
+    for t, n in ((key_out, "key_out"), (value_out, "value_out")):
         _require(t, n, key_cache.dtype)
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
+        _require(t, n, key_cache.dtype, dense=False)
+    layout = kv_layout_of(key_cache, value_cache)
     _require(slot_mapping, "slot_mapping", torch.int32)
     NB, Hkv, BS, D = key_cache.shape
     check(lib().gather_cached_kv(
         key_out.data_ptr(), value_out.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         slot_mapping.data_ptr(), slot_mapping.shape[0], Hkv, D, int(block_size), NB,
-        _DTYPE[key_cache.dtype], _stream_ptr(stream)))
+        _DTYPE[key_cache.dtype], layout, _stream_ptr(stream)))
     return key_out, value_out
 
 
@@ -171,17 +207,20 @@ def paged_kv_cache_write(key_cache: torch.Tensor, value_cache: torch.Tensor, key
                          value: torch.Tensor, slot_mapping: torch.Tensor, block_size: int,
                          stream=None):
     """Enqueue the bit-exact store of key/value rows ([T, Hkv, D]) into their cache slots."""
-    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache"), (key, "key"),
-                 (value, "value")):
+    for t, n in ((key, "key"), (value, "value")):
         _require(t, n, key_cache.dtype)
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
+        _require(t, n, key_cache.dtype, dense=False)
+    layout = kv_layout_of(key_cache, value_cache)
     _require(slot_mapping, "slot_mapping", torch.int32)
     NB, Hkv, BS, D = key_cache.shape
     check(lib().paged_kv_cache_write(
         key_cache.data_ptr(), value_cache.data_ptr(), key.data_ptr(), value.data_ptr(),
         slot_mapping.data_ptr(), slot_mapping.shape[0], Hkv, D, int(block_size), NB,
-        _DTYPE[key_cache.dtype], _stream_ptr(stream)))
+        _DTYPE[key_cache.dtype], layout, _stream_ptr(stream)))
     return key_cache, value_cache
 
 
 __all__ = ["paged_attention_decode", "paged_attention_plan", "paged_attention_workspace_bytes",
-           "paged_attention_prefill", "make_prefill_dims", "gather_cached_kv", "paged_kv_cache_write", "make_dims", "make_opts", "_lib"]
+           "paged_attention_prefill", "make_prefill_dims", "gather_cached_kv", "paged_kv_cache_write",
+           "make_dims", "make_opts", "joint_kv_cache", "kv_layout_of", "_lib"]

@@ -63,6 +63,22 @@ typedef enum {
   PA_KV_FP8_E4M3 = 1 /* caches hold FP8 E4M3 codes; value = code * k/v_scale   */
 } pa_kv_format;
 
+/* Where K and V tiles sit relative to each other.  A tile is the block_size x
+ * head_size slab of one (physical block, kv head); every layout keeps a tile
+ * contiguous, rows of head_size elements.
+ *   PA_KV_SEPARATE  two tensors, key_cache and value_cache, each
+ *                   [num_blocks, num_kv_heads, block_size, head_size].
+ *   PA_KV_JOINT     one tensor [num_blocks, num_kv_heads, 2, block_size,
+ *                   head_size]: the K tile of (block, kv head) followed by its
+ *                   V tile.  key_cache points at the first K tile and
+ *                   value_cache at the first V tile, i.e. value_cache must be
+ *                   key_cache + block_size * head_size elements.
+ * Results do not depend on the layout.  The joint layout reads each
+ * (block, kv head) as one contiguous run of K and V; on MI355X it measured
+ * faster for decode than two tensors at whatever relative address the
+ * allocator gives them. */
+typedef enum { PA_KV_SEPARATE = 0, PA_KV_JOINT = 1 } pa_kv_layout;
+
 /* Status codes. */
 enum {
   PA_OK = 0,
@@ -77,8 +93,8 @@ enum {
 /* Shapes of one decode call.
  *   query        [num_seqs, num_heads, head_size]                     dtype
  *   out          [num_seqs, num_heads, head_size]                     dtype
- *   key_cache    [num_blocks, num_kv_heads, block_size, head_size]    dtype
- *   value_cache  [num_blocks, num_kv_heads, block_size, head_size]    dtype
+ *   key_cache    [num_blocks, num_kv_heads, block_size, head_size]    dtype   (strides
+ *   value_cache  [num_blocks, num_kv_heads, block_size, head_size]    dtype    per kv_layout)
  *   block_tables [num_seqs, max_blocks_per_seq]                       int32
  *   context_lens [num_seqs]                                           int32
  *   alibi_slopes [num_heads]                                          float32, or NULL
@@ -100,6 +116,7 @@ typedef struct {
   float k_scale;     /* FP8 caches: real key = code * k_scale (finite, > 0)    */
   float v_scale;     /* FP8 caches: real value = code * v_scale; both ignored
                         for native caches                                      */
+  int32_t kv_layout; /* pa_kv_layout; 0 (separate) when zero-initialised     */
 } pa_dims;
 
 /* Which inner engine computes q.K and p.V. */
@@ -235,7 +252,8 @@ int paged_attention_prefill_plan(const pa_dims* dims, int32_t num_query_tokens,
  * num_tokens, num_heads, head_size, block_size and num_blocks).
  *
  * key_out, value_out  [num_tokens, num_kv_heads, head_size]            dtype
- * key_cache, value_cache [num_blocks, num_kv_heads, block_size, head_size] dtype
+ * key_cache, value_cache [num_blocks, num_kv_heads, block_size, head_size] dtype,
+ *                     laid out as kv_layout says (pa_kv_layout)
  * slot_mapping        [num_tokens] int32; slot = block * block_size + offset.
  *                     A negative slot writes a zero row.  Slots must be
  *                     < num_blocks * block_size (device-side precondition).
@@ -246,7 +264,7 @@ int paged_attention_prefill_plan(const pa_dims* dims, int32_t num_query_tokens,
 int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
                      const void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
                      int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                     int32_t num_blocks, int32_t dtype, pa_stream_t stream);
+                     int32_t num_blocks, int32_t dtype, int32_t kv_layout, pa_stream_t stream);
 
 /*
  * paged_kv_cache_write -- store the K/V rows of new tokens into their cache
@@ -254,7 +272,8 @@ int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
  * (vLLM PR #2744 discusses its cost at large block sizes).  Inverse of
  * gather_cached_kv.
  *
- * key_cache, value_cache [num_blocks, num_kv_heads, block_size, head_size] dtype (written)
+ * key_cache, value_cache [num_blocks, num_kv_heads, block_size, head_size] dtype (written),
+ *                        laid out as kv_layout says (pa_kv_layout)
  * key, value             [num_tokens, num_kv_heads, head_size]             dtype
  * slot_mapping           [num_tokens] int32; slot = block * block_size + offset.
  *                        A negative slot (a padding token) stores nothing.
@@ -267,7 +286,7 @@ int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
 int paged_kv_cache_write(void* key_cache, void* value_cache, const void* key, const void* value,
                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                          int32_t head_size, int32_t block_size, int32_t num_blocks, int32_t dtype,
-                         pa_stream_t stream);
+                         int32_t kv_layout, pa_stream_t stream);
 
 /* Static description of a status code. */
 const char* pa_status_string(int status);

@@ -1,0 +1,148 @@
+"""GPU parity with the caches in the joint layout [NB, Hkv, 2, BS, D].
+
+The inputs hold the same bytes as the separate-tensor layout of the same seed
+(the generator lays the same draws out both ways), so every result is checked
+twice: against the fp64 oracle within the usual tolerance (max abs 2e-3 fp16,
+1e-2 bf16; bit-exact for the row copies) and bit for bit against the call on
+two separate cache tensors.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_paged_06_amd import (gather_cached_kv, joint_kv_cache, kv_layout_of,
+                                           paged_attention_prefill, paged_kv_cache_write)
+from decode_attention_paged_06_amd._lib import PA_KV_JOINT, PA_KV_SEPARATE
+from gpu_util import compare, device, make, oracle_ref, run, sample_seqs
+from workloads import gather_inputs, prefill_inputs, raw_bits, raw_u16, workload_args
+
+pytestmark = pytest.mark.gpu
+
+
+def both_layouts(**kw):
+    dev = device()
+    sep = make(device_=dev, kv_layout="separate", **kw)
+    joint = make(device_=dev, kv_layout="joint", **kw)
+    assert kv_layout_of(sep.key_cache, sep.value_cache) == PA_KV_SEPARATE
+    assert kv_layout_of(joint.key_cache, joint.value_cache) == PA_KV_JOINT
+    assert torch.equal(sep.key_cache.view(torch.uint8), joint.key_cache.view(torch.uint8))
+    assert torch.equal(sep.value_cache.view(torch.uint8), joint.value_cache.view(torch.uint8))
+    return sep, joint
+
+
+DECODE_CASES = [
+    # (id, kwargs, engines, partition sizes)
+    ("gqa-bf16", dict(num_seqs=5, num_heads=64, num_kv_heads=8, head_size=128, block_size=16,
+                      dtype="bf16", context_lens=[1, 17, 300, 1000, 64], alibi=False),
+     ("mfma", "valu"), (-1, 0, 64)),
+    ("mha-f16-d64", dict(num_seqs=4, num_heads=4, num_kv_heads=4, head_size=64, block_size=16,
+                         dtype="f16", context_lens=(1, 64), pool_blocks=64, alibi=False),
+     ("valu", "mfma"), (-1, 16)),
+    ("mqa48-alibi", dict(num_seqs=6, num_heads=48, num_kv_heads=1, head_size=128, block_size=16,
+                         dtype="f16", context_lens=[64, 900, 3, 2000, 129, 511], alibi=True),
+     ("mfma", "valu"), (-1, 0, 256)),
+    ("gqa-fp8", dict(num_seqs=4, num_heads=16, num_kv_heads=2, head_size=128, block_size=16,
+                     dtype="bf16", context_lens=[33, 700, 1, 260], alibi=True, kv_dtype="fp8"),
+     ("mfma", "valu"), (-1, 64)),
+    ("mqa32-fp8", dict(num_seqs=3, num_heads=32, num_kv_heads=1, head_size=128, block_size=16,
+                       dtype="f16", context_lens=[400, 90, 1500], alibi=False, kv_dtype="fp8"),
+     ("mfma",), (-1, 0, 128)),
+    ("block8", dict(num_seqs=4, num_heads=16, num_kv_heads=2, head_size=128, block_size=8,
+                    dtype="bf16", context_lens=[7, 8, 9, 333], alibi=True),
+     ("mfma", "valu"), (-1, 64)),
+    ("block256", dict(num_seqs=3, num_heads=16, num_kv_heads=2, head_size=64, block_size=256,
+                      dtype="f16", context_lens=[255, 257, 900], alibi=False),
+     ("mfma", "valu"), (-1, 256)),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_joint_layout(case):
+    name, kw, engines, partitions = case
+    sep, joint = both_layouts(seed=len(name) * 31, poison=True, **kw)
+    ref = oracle_ref(sep)
+    for engine in engines:
+        for ps in partitions:
+            a = run(sep, engine=engine, partition_size=ps)
+            b = run(joint, engine=engine, partition_size=ps)
+            what = f"{name} joint {engine} partition={ps}"
+            compare(b, ref, sep.dtype, what=what)
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{what}: differs from separate"
+
+
+@pytest.mark.parametrize("name,batch,kv", [("gqa_ctx4096", 256, None), ("gqa_ctx4096", 256, "fp8"),
+                                           ("mqa_ragged_alibi", 256, None)])
+def test_bench_shapes_joint_layout(name, batch, kv):
+    """The bench's workloads in the joint layout at full size, auto plan (sampled rows)."""
+    args = workload_args(name, batch)
+    if kv:
+        args["kv_dtype"] = kv
+    dev = device()
+    joint = make(device_=dev, kv_layout="joint", **args)
+    seqs = sample_seqs(batch, 16, seed=batch + 5)
+    ref = oracle_ref(joint, seqs)
+    compare(run(joint), ref, joint.dtype, seqs, what=f"{name} b={batch} kv={kv} joint")
+
+
+def test_prefill_joint_layout():
+    dev = device()
+    kw = dict(num_seqs=3, num_heads=16, num_kv_heads=2, head_size=128, block_size=16, dtype="bf16",
+              context_lens=[300, 45, 129], alibi=True, poison=True)
+    news = [64, 45, 1]
+    outs = []
+    for layout in ("separate", "joint"):
+        inp, q, qs, max_q = prefill_inputs(new_tokens=news, seed=808, device=dev, kv_layout=layout, **kw)
+        for ps in (0, 64):
+            out = torch.full_like(q, float("nan"))
+            paged_attention_prefill(out, q, inp.key_cache, inp.value_cache, inp.block_tables,
+                                    inp.context_lens, qs, max_q, inp.scale, inp.block_size,
+                                    inp.alibi_slopes, partition_size=ps)
+            torch.cuda.synchronize()
+            outs.append(out)
+        if layout == "joint":
+            ref = oracle.paged_prefill(raw_u16(q), raw_bits(inp.key_cache), raw_bits(inp.value_cache),
+                                       inp.block_tables.cpu().numpy(), inp.context_lens.cpu().numpy(),
+                                       qs.cpu().numpy(), inp.scale, inp.block_size,
+                                       inp.alibi_slopes.cpu().numpy(), dtype=inp.dtype)
+            for out in outs[2:]:
+                compare(out, ref, "bf16", what="prefill joint")
+    for a, b in zip(outs[:2], outs[2:]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("case", [(2048, 40, 128, 8, 1024, "f16", 0), (333, 8, 128, 16, 256, "bf16", 5),
+                                  (17, 3, 8, 5, 11, "bf16", 2)],
+                         ids=["gather-page-shape", "bf16-neg", "tiny-odd"])
+def test_gather_and_write_joint_layout(case):
+    dev = device()
+    T, H, D, BS, NB, dtype, neg = case
+    g = gather_inputs(num_tokens=T, num_kv_heads=H, head_size=D, block_size=BS, num_blocks=NB,
+                      dtype=dtype, seed=3 * T + H, random_bits=True, num_negative=neg, device=dev,
+                      kv_layout="joint")
+    assert kv_layout_of(g.key_cache, g.value_cache) == PA_KV_JOINT
+    ko = torch.empty((T, H, D), dtype=g.key_cache.dtype, device=dev)
+    vo = torch.empty_like(ko)
+    ko.view(torch.int16).fill_(0x5555)
+    vo.view(torch.int16).fill_(0x5555)
+    gather_cached_kv(ko, vo, g.key_cache, g.value_cache, g.slot_mapping, BS)
+    torch.cuda.synchronize()
+    slots = g.slot_mapping.cpu().numpy()
+    rk, rv = oracle.gather_cached_kv(raw_u16(g.key_cache), raw_u16(g.value_cache), slots, BS)
+    assert np.array_equal(raw_u16(ko), rk) and np.array_equal(raw_u16(vo), rv)
+
+    # write new rows into a fresh joint cache holding the same bytes, check
+    # against the oracle's write, and that K writes never touch V tiles
+    kc, vc = joint_kv_cache(NB, H, BS, D, g.key_cache.dtype, dev)
+    kc.copy_(g.key_cache)
+    vc.copy_(g.value_cache)
+    gen = torch.Generator(device=dev).manual_seed(T)
+    nk = torch.randint(-32768, 32768, (T, H, D), generator=gen, dtype=torch.int32,
+                       device=dev).to(torch.int16).view(kc.dtype)
+    nv = torch.randint(-32768, 32768, (T, H, D), generator=gen, dtype=torch.int32,
+                       device=dev).to(torch.int16).view(kc.dtype)
+    paged_kv_cache_write(kc, vc, nk, nv, g.slot_mapping, BS)
+    torch.cuda.synchronize()
+    wk, wv = oracle.kv_cache_write(raw_u16(g.key_cache), raw_u16(g.value_cache), raw_u16(nk),
+                                   raw_u16(nv), slots, BS)
+    assert np.array_equal(raw_u16(kc), wk) and np.array_equal(raw_u16(vc), wv)

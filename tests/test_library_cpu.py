@@ -159,8 +159,8 @@ def test_fp8_cache_validation(L):
     d.kv_format = 3
     assert plan(L, d)[0] == UNSUPPORTED
     g = L.gather_cached_kv               # fp8 rows of head size 8 are 8 bytes: not 16-byte rows
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 8, 16, 10, 2, None) == UNSUPPORTED
-    assert g(None, None, None, None, None, 0, 8, 16, 16, 10, 2, None) == OK
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 8, 16, 10, 2, 0, None) == UNSUPPORTED
+    assert g(None, None, None, None, None, 0, 8, 16, 16, 10, 2, 0, None) == OK
 
 
 def test_prefill_validation(L):
@@ -221,29 +221,48 @@ def test_decode_validation(L):
 
 def test_gather_validation(L):
     g = L.gather_cached_kv
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 5, None) == UNSUPPORTED
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 12, 16, 10, 0, None) == UNSUPPORTED
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 128, 16, 10, 0, None) == INVALID
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0, 128, 16, 10, 0, None) == INVALID
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 0, 10, 0, None) == INVALID
-    assert g(None, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 0, None) == INVALID
-    assert g(FAKE + 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 0, None) == ALIGN
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 4, 8, 128, 16, 10, 0, None) == ALIGN
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 64, 128, 16, 10, 0, None) == INVALID
-    assert g(None, None, None, None, None, 0, 8, 128, 16, 10, 0, None) == OK
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 5, 0, None) == UNSUPPORTED
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 12, 16, 10, 0, 0, None) == UNSUPPORTED
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 128, 16, 10, 0, 0, None) == INVALID
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0, 128, 16, 10, 0, 0, None) == INVALID
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 0, 10, 0, 0, None) == INVALID
+    assert g(None, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 0, 0, None) == INVALID
+    assert g(FAKE + 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 0, 0, None) == ALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 4, 8, 128, 16, 10, 0, 0, None) == ALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 64, 128, 16, 10, 0, 0, None) == INVALID
+    assert g(None, None, None, None, None, 0, 8, 128, 16, 10, 0, 0, None) == OK
 
 
 def test_cache_write_validation(L):
     w = L.paged_kv_cache_write
-    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 9, None) == UNSUPPORTED
-    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 100, 16, 10, 0, None) == UNSUPPORTED
-    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, -2, 8, 128, 16, 10, 0, None) == INVALID
-    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 0, 0, None) == INVALID
-    assert w(FAKE, None, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 0, None) == INVALID
-    assert w(FAKE, FAKE, FAKE + 8, FAKE, FAKE, 4, 8, 128, 16, 10, 0, None) == ALIGN
-    assert w(FAKE, FAKE, FAKE, FAKE, FAKE + 1, 4, 8, 128, 16, 10, 0, None) == ALIGN
-    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 1 << 20, 1 << 12, 0, None) == INVALID
-    assert w(None, None, None, None, None, 0, 8, 128, 16, 10, 1, None) == OK
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 9, 0, None) == UNSUPPORTED
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 100, 16, 10, 0, 0, None) == UNSUPPORTED
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, -2, 8, 128, 16, 10, 0, 0, None) == INVALID
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 0, 0, 0, None) == INVALID
+    assert w(FAKE, None, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 0, 0, None) == INVALID
+    assert w(FAKE, FAKE, FAKE + 8, FAKE, FAKE, 4, 8, 128, 16, 10, 0, 0, None) == ALIGN
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE + 1, 4, 8, 128, 16, 10, 0, 0, None) == ALIGN
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 1 << 20, 1 << 12, 0, 0, None) == INVALID
+    assert w(None, None, None, None, None, 0, 8, 128, 16, 10, 1, 0, None) == OK
+
+
+def test_kv_layout_validation(L):
+    d = dims()
+    d.kv_layout = 2                      # neither separate nor joint
+    assert plan(L, d)[0] == INVALID
+    tile = 16 * 128 * 2                  # block_size * head_size * 2 bytes
+    d = dims()
+    d.kv_layout = 1                      # joint: value tiles must follow key tiles
+    assert plan(L, d)[0] == OK
+    assert decode(L, d, k=FAKE, v=FAKE + 2 * tile) == INVALID
+    assert "joint" in L.pa_last_error().decode()
+    assert decode(L, d, k=FAKE + 4 * tile, v=FAKE) == INVALID
+    g, w = L.gather_cached_kv, L.paged_kv_cache_write
+    for f in (g, w):
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 0, 7, None) == INVALID
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 0, 1, None) == INVALID
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 1, 1, None) == INVALID
+        assert f(None, None, None, None, None, 0, 8, 128, 16, 10, 0, 1, None) == OK
 
 
 def test_plan_block_sizes(L):
@@ -331,3 +350,26 @@ def test_last_error_is_per_thread(L):
     for th in threads:
         th.join()
     assert not failures, failures[:3]
+
+
+def test_binding_detects_cache_layout():
+    import torch
+
+    from decode_attention_paged_06_amd import kv_layout_of
+
+    NB, Hkv, BS, D = 5, 3, 16, 64
+    k = torch.zeros((NB, Hkv, BS, D), dtype=torch.float16)
+    v = torch.zeros_like(k)
+    assert kv_layout_of(k, v) == 0
+    kv = torch.zeros((NB, Hkv, 2, BS, D), dtype=torch.bfloat16)
+    assert kv_layout_of(kv[:, :, 0], kv[:, :, 1]) == 1
+    with pytest.raises(ValueError):       # V tiles must follow K tiles
+        kv_layout_of(kv[:, :, 1], kv[:, :, 0])
+    kv16 = torch.zeros((NB, Hkv, 2, BS, D), dtype=torch.float16)
+    with pytest.raises(ValueError):       # one dense, one strided
+        kv_layout_of(k, kv16[:, :, 1])
+    kv2 = torch.zeros((NB, 2, Hkv, BS, D), dtype=torch.float16)
+    with pytest.raises(ValueError):       # [NB, 2, Hkv, BS, D] is not a supported layout
+        kv_layout_of(kv2[:, 0], kv2[:, 1])
+    with pytest.raises(ValueError):
+        kv_layout_of(k, v[:, :, :8])

@@ -7,8 +7,10 @@ identical bytes for identical seeds and devices.
 
 Layout (the contract of the library in ``include/paged_attention.h``):
   query        [S, Hq, D]            fp16 or bf16
-  key_cache    [NB, Hkv, BS, D]      fp16 or bf16
-  value_cache  [NB, Hkv, BS, D]      fp16 or bf16
+  key_cache    [NB, Hkv, BS, D]      fp16 or bf16 (or fp8)
+  value_cache  [NB, Hkv, BS, D]      fp16 or bf16 (or fp8)
+               two dense tensors, or (kv_layout="joint") the K and V views of
+               one [NB, Hkv, 2, BS, D] tensor holding the same bytes
   block_tables [S, MAXB]             int32, physical block ids
   context_lens [S]                   int32
   alibi_slopes [Hq]                  fp32 (optional)
@@ -105,7 +107,7 @@ def decode_inputs(*, num_seqs: int, num_heads: int, num_kv_heads: int, head_size
                   pool_blocks: Optional[int] = None, max_blocks_per_seq: Optional[int] = None,
                   alibi: bool = False, scale: Optional[float] = None, poison: bool = False,
                   device: Union[str, torch.device] = "cpu", kv_dtype: Optional[str] = None,
-                  kv_scale: float = 0.0625) -> DecodeInputs:
+                  kv_scale: float = 0.0625, kv_layout: str = "separate") -> DecodeInputs:
     """Build one seeded decode batch.
 
     pool_blocks=None sizes the pool to fit exactly the blocks the sequences
@@ -115,6 +117,9 @@ def decode_inputs(*, num_seqs: int, num_heads: int, num_kv_heads: int, head_size
     kv_dtype="fp8" stores K and V as FP8 E4M3 with one scale per cache:
     the real value is code * kv_scale (draws are divided by kv_scale before
     rounding, so the real values stay ~N(0, 1)).
+
+    kv_layout="joint" returns K and V as the two views of one [NB, Hkv, 2, BS,
+    D] tensor (same values as "separate").
 
     poison=True writes NaN into every cache slot no valid token occupies
     (tail slots of each last block and all unused pool blocks) and points
@@ -165,6 +170,7 @@ def decode_inputs(*, num_seqs: int, num_heads: int, num_kv_heads: int, head_size
                 kc[last, :, tail:, :] = nan
                 vc[last, :, tail:, :] = nan
 
+    kc, vc = _lay_out(kc, vc, kv_layout)
     slopes = alibi_slopes_geometric(num_heads).to(device) if alibi else None
     if scale is None:
         scale = 1.0 / math.sqrt(head_size)
@@ -174,6 +180,15 @@ def decode_inputs(*, num_seqs: int, num_heads: int, num_kv_heads: int, head_size
                         dtype=dtype, seed=seed, num_blocks_used=used,
                         poison_block=poison_block, kv_dtype=kv_dtype, k_scale=kv_s,
                         v_scale=kv_s)
+
+
+def _lay_out(kc: torch.Tensor, vc: torch.Tensor, kv_layout: str):
+    """The caches as two dense tensors, or as the K and V views of one joint tensor."""
+    if kv_layout == "separate":
+        return kc, vc
+    assert kv_layout == "joint", kv_layout
+    kv = torch.stack([kc, vc], dim=2)   # [NB, Hkv, 2, BS, D], dense
+    return kv[:, :, 0], kv[:, :, 1]
 
 
 @dataclass
@@ -188,7 +203,8 @@ class GatherInputs:
 
 def gather_inputs(*, num_tokens: int, num_kv_heads: int, head_size: int, block_size: int,
                   num_blocks: int, dtype: str, seed: int, random_bits: bool = False,
-                  num_negative: int = 0, device: Union[str, torch.device] = "cpu") -> GatherInputs:
+                  num_negative: int = 0, device: Union[str, torch.device] = "cpu",
+                  kv_layout: str = "separate") -> GatherInputs:
     """Pool plus a slot mapping of distinct random slots.
 
     random_bits=True fills the pool with uniformly random 16-bit patterns
@@ -213,6 +229,7 @@ def gather_inputs(*, num_tokens: int, num_kv_heads: int, head_size: int, block_s
     else:
         kc = _randn(shape, dtype, dev, device)
         vc = _randn(shape, dtype, dev, device)
+    kc, vc = _lay_out(kc, vc, kv_layout)
     return GatherInputs(key_cache=kc, value_cache=vc, slot_mapping=slots.to(device),
                         block_size=block_size, dtype=dtype, seed=seed)
 
