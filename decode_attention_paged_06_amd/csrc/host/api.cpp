@@ -40,11 +40,17 @@ constexpr int kMaxDevices = 64;
 // workgroups: two partitions of 4096 tokens measured best, 121 us against 134
 // with four).  The VALU engine: one (its split costs more than the grid fill
 // gains on the 40-head MHA batch: 320 workgroups run best as one pass).
+// One-head-tile decode over an FP8 cache: two per CU, in partitions of at
+// least 128 tokens -- its register tiles are half the bytes, so a workgroup
+// keeps fewer bytes in flight (GQA 64/8 context 4096, graph replay: batch 16
+// 41.2 -> 30.8 us, batch 4 15.2 -> 14.6 us; context 1024 batch 16 16.1 ->
+// 15.3 us; batch 1 at context 1024 8.4 -> 8.8 us).
 constexpr int kTargetGroupsPerCu = 2;
 constexpr int kTargetGroupsPerCuOneTile = 1;
+constexpr int kTargetGroupsPerCuOneTileFp8 = 2;
 constexpr int kTargetGroupsPerCuValu = 1;
 // Smallest partition the auto plan makes: 128 tokens (two 16-row tiles per
-// wave), 64 for one-head-tile decode.
+// wave), 64 for one-head-tile decode over a 16-bit cache.
 constexpr int kMinPartitionTokens = 128;
 constexpr int kMinPartitionTokensOneTile = 64;
 
@@ -231,10 +237,12 @@ int make_plan(const pa_dims* d, const CallShape& c, size_t ws_bytes, const pa_op
     if (cus == 0 && (st = current_num_cus(&cus))) return st;
     const long long units = (long long)d->num_seqs * d->num_kv_heads * row_chunks(d, c, engine);
     const bool one_tile = engine == PA_ENGINE_MFMA && !c.multi && pa::mfma_head_tiles(group) == 1;
+    const bool fp8 = d->kv_format == PA_KV_FP8_E4M3;
     const long long target = (long long)(engine == PA_ENGINE_VALU ? kTargetGroupsPerCuValu
+                                         : one_tile && fp8         ? kTargetGroupsPerCuOneTileFp8
                                          : one_tile                ? kTargetGroupsPerCuOneTile
                                                                    : kTargetGroupsPerCu) * cus;
-    const int min_tokens = one_tile ? kMinPartitionTokensOneTile : kMinPartitionTokens;
+    const int min_tokens = one_tile && !fp8 ? kMinPartitionTokensOneTile : kMinPartitionTokens;
     const int min_pb = min_tokens / d->block_size > 1 ? min_tokens / d->block_size : 1;
     if (units > 0 && units < target && maxb > min_pb) {
       long long want = (target + units - 1) / units;

@@ -283,6 +283,13 @@ def test_plan_one_tile_targets_one_group_per_cu(L):
     # a 48-head group (three tiles) keeps two workgroups per CU
     st, p = plan(L, dims(S=64, Hq=48, Hkv=1, MAXB=256))
     assert st == OK and p.num_partitions == 8
+    # over an FP8 cache: two per CU, partitions of 128+ tokens
+    for S, maxb, P in ((1, 256, 32), (4, 256, 16), (16, 256, 4), (1, 64, 8), (4, 64, 8),
+                       (16, 64, 4), (64, 256, 1)):
+        d = dims(S=S, MAXB=maxb)
+        d.kv_format, d.k_scale, d.v_scale = 1, 0.5, 0.5
+        st, p = plan(L, d)
+        assert st == OK and p.engine == 2 and p.num_partitions == P, (S, maxb, p.num_partitions)
 
 
 def test_plan_multi_tile_partitions(L):
