@@ -60,6 +60,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hot", action="store_true",
+                    help="time one input set over and over (no rotation): a labelled hot-cache "
+                         "figure for workloads that fit the last-level cache")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the device-copy / streaming-read ceiling measured after the timed region")
     ap.add_argument("--graph", action="store_true",
                     help="also time the calls replayed from a HIP graph (GPU time without the "
                          "host launch path; matters for small, launch-bound batches)")
@@ -256,6 +261,48 @@ def calibrate_copy(mib, steps):
                       "bytes_written_per_copy": n, "copies": steps}), flush=True)
 
 
+def device_ceiling(gib: int = 4, reps: int = 10):
+    """What plain device-wide streaming reaches on this GPU, as context for the
+    kernel's fraction of the vendor peak: the library's streaming-read probe
+    over `gib` GiB (the decode kernels' 16-byte non-temporal loads, contiguous
+    runs, reads only) and a device-to-device copy of 1 GiB (the runtime's copy
+    kernel, read and written)."""
+    import torch
+
+    from decode_attention_paged_06_amd.ops import stream_read_probe
+
+    n = gib << 30
+    big = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    sink = stream_read_probe(big)
+    src, dst = big[: 1 << 30], torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(2):
+        stream_read_probe(big, sink)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e[0].record()
+    for _ in range(reps):
+        stream_read_probe(big, sink)
+    e[1].record()
+    e[2].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e[3].record()
+    torch.cuda.synchronize()
+    read_s = e[0].elapsed_time(e[1]) * 1e-3 / reps
+    copy_s = e[2].elapsed_time(e[3]) * 1e-3 / reps
+    del big, sink, src, dst
+    torch.cuda.empty_cache()
+    read_gbps = n / read_s / 1e9
+    copy_gbps = 2 * (1 << 30) / copy_s / 1e9
+    return {"stream_read_GB/s": round(read_gbps, 1),
+            "stream_read_pct_of_peak": round(100 * read_gbps / HBM_PEAK_GBPS, 1),
+            "copy_GB/s_read_plus_write": round(copy_gbps, 1),
+            "copy_pct_of_peak": round(100 * copy_gbps / HBM_PEAK_GBPS, 1),
+            "note": f"streaming-read probe over {gib} GiB and torch copy_ of 1 GiB, {reps} each, "
+                    f"after the timed region"}
+
+
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -395,7 +442,7 @@ def main():
                               head_size=args["head_size"])
     footprint = sum(t.numel() * t.element_size() for t in
                     (first.query, first.key_cache, first.value_cache, first.block_tables))
-    nsets = max(1, -(-ROTATE_BYTES // footprint))
+    nsets = 1 if a.hot else max(1, -(-ROTATE_BYTES // footprint))
     sets = [first]
     for i in range(1, nsets):
         # same lengths and shapes, fresh values and block assignment
@@ -439,6 +486,9 @@ def main():
 
     per_call_ms = [s.elapsed_time(e) for s, e in ev]
     avg_ms = sum(per_call_ms) / len(per_call_ms)
+    srt = sorted(per_call_ms)
+    per_call_us = {"median": round(srt[len(srt) // 2] * 1e3, 2), "min": round(srt[0] * 1e3, 2),
+                   "max": round(srt[-1] * 1e3, 2)}
     region_ms = t_start.elapsed_time(t_end)
     ms_per_step = region_ms / a.steps
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -473,6 +523,8 @@ def main():
         torch.cuda.synchronize()
         graph_us = g0.elapsed_time(g1) * 1e3 / (reps * ncap)
 
+    ceiling = None if a.no_ceiling else device_ceiling()
+
     kernel_name = "decode_mfma_kernel" if plan.engine == 2 else "decode_valu_kernel"
     context = PAGES_US.get((name, batch))
     vs = None
@@ -502,7 +554,9 @@ def main():
             "num_partitions": plan.num_partitions, "partition_size": plan.partition_size,
             "schedule": {2: "longest_first"}.get(plan.schedule, "grid"),
             "input_sets_rotated": nsets,
+            **({"hot_cache": True} if a.hot else {}),
         },
+        "per_call_us": per_call_us,
         "us_per_call": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_call": nbytes,
@@ -528,6 +582,8 @@ def main():
                                   "GB/s": round(nbytes / (graph_us * 1e-6) / 1e9, 2),
                                   "pct_of_hbm_peak": round(100 * nbytes / (graph_us * 1e-6) / 1e9
                                                            / HBM_PEAK_GBPS, 2)}
+    if ceiling is not None:
+        result["device_ceiling"] = ceiling
     if context:
         result["pages_context"] = dict(context, note="A100 numbers from the reference pages; "
                                        "vs_baseline = FlashAttention A100 us / this us")

@@ -23,7 +23,7 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_E
 EXPORTS = ("paged_attention_decode", "paged_attention_workspace_bytes", "paged_attention_plan",
            "paged_attention_prefill", "paged_attention_prefill_workspace_bytes",
            "paged_attention_prefill_plan", "gather_cached_kv", "paged_kv_cache_write",
-           "pa_status_string", "pa_last_error")
+           "pa_status_string", "pa_last_error", "pa_stream_read_probe", "pa_stream_read_sink_bytes")
 
 
 class PaDims(ctypes.Structure):
@@ -86,6 +86,10 @@ def lib() -> ctypes.CDLL:
     L.gather_cached_kv.restype = ctypes.c_int
     L.paged_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     L.paged_kv_cache_write.restype = ctypes.c_int
+    L.pa_stream_read_probe.argtypes = [vp, sz, vp, sz, vp]
+    L.pa_stream_read_probe.restype = ctypes.c_int
+    L.pa_stream_read_sink_bytes.argtypes = [sz]
+    L.pa_stream_read_sink_bytes.restype = sz
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_last_error.argtypes = []

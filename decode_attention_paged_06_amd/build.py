@@ -27,6 +27,7 @@ SOURCES = [
     "kernels/reduce.hip",
     "kernels/gather.hip",
     "kernels/schedule.hip",
+    "kernels/probe.hip",
 ]
 
 ARCH = "gfx950"

@@ -98,4 +98,11 @@ hipError_t launch_cache_write(void* k_cache, void* v_cache, const void* k_new, c
                               int32_t row_bytes, int32_t block_size, int64_t block_stride,
                               int64_t head_stride, hipStream_t s);
 
+// Streaming-read probe: reads `bytes` (a multiple of 16) at `src` once;
+// `sink` holds stream_read_grid(bytes) 16-byte slots (practically never
+// written).  At most kStreamReadMaxBlocks workgroups of 256 threads.
+constexpr int kStreamReadMaxBlocks = 4096;
+int stream_read_grid(size_t bytes);
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
+
 }  // namespace pa

@@ -221,6 +221,20 @@ def paged_kv_cache_write(key_cache: torch.Tensor, value_cache: torch.Tensor, key
     return key_cache, value_cache
 
 
+def stream_read_probe(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None):
+    """Enqueue one streaming read of ``src``'s bytes (a measurement aid; see
+    pa_stream_read_probe).  Returns the sink tensor (allocated when omitted)."""
+    _require(src, "src")
+    nbytes = src.numel() * src.element_size()
+    need = int(lib().pa_stream_read_sink_bytes(nbytes))
+    if sink is None:
+        sink = torch.empty(max(need, 16), dtype=torch.uint8, device=src.device)
+    _require(sink, "sink")
+    check(lib().pa_stream_read_probe(src.data_ptr(), nbytes, sink.data_ptr(),
+                                     sink.numel() * sink.element_size(), _stream_ptr(stream)))
+    return sink
+
+
 __all__ = ["paged_attention_decode", "paged_attention_plan", "paged_attention_workspace_bytes",
            "paged_attention_prefill", "make_prefill_dims", "gather_cached_kv", "paged_kv_cache_write",
-           "make_dims", "make_opts", "joint_kv_cache", "kv_layout_of", "_lib"]
+           "make_dims", "make_opts", "joint_kv_cache", "kv_layout_of", "stream_read_probe", "_lib"]

@@ -380,3 +380,15 @@ def test_binding_detects_cache_layout():
         kv_layout_of(kv2[:, 0], kv2[:, 1])
     with pytest.raises(ValueError):
         kv_layout_of(k, v[:, :, :8])
+
+
+def test_stream_read_probe_validation(L):
+    p = L.pa_stream_read_probe
+    assert L.pa_stream_read_sink_bytes(0) == 0
+    assert L.pa_stream_read_sink_bytes(16 * 2048) == 16            # one workgroup per 32 KB
+    assert L.pa_stream_read_sink_bytes(1 << 32) == 16 * 4096      # grid capped at 4096 workgroups
+    assert p(FAKE, 24, FAKE, 1 << 20, None) == INVALID              # not a multiple of 16
+    assert p(None, 1024, FAKE, 1 << 20, None) == INVALID
+    assert p(FAKE + 8, 1024, FAKE, 1 << 20, None) == ALIGN
+    assert p(FAKE, 1 << 20, FAKE, 16, None) == INVALID              # sink too small
+    assert p(None, 0, None, 0, None) == OK
