@@ -56,19 +56,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
   const int nh = min(GT, a.group - hc * GT);
   const bool single = a.num_partitions == 1;
 
-  const int L = min(a.context_lens[seq], a.max_blocks_per_seq * BS);
   const int tok0 = part * a.partition_blocks * BS;
-  if (L <= 0) {
-    if (single) {
-      uint4* o = reinterpret_cast<uint4*>(a.out) + ((size_t)seq * a.num_heads + h0) * CH;
-      for (int i = threadIdx.x; i < nh * CH; i += kWaves * 64) o[i] = make_uint4(0, 0, 0, 0);
-    }
-    return;
-  }
-  if (tok0 >= L) return;  // partition past this sequence's end: nothing to do
-  const int tok1 = min(L, tok0 + a.partition_blocks * BS);
-  const int tile0 = tok0 / TT;
-  const int ntiles = (tok1 - tok0 + TT - 1) / TT;
+  const int tile0 = tok0 / TT;  // first tile of the partition
+  const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+
+  // The context length, the block ids of this wave's first two tiles (their
+  // table positions do not depend on the context length; clamped to the
+  // table row) and the query are requested together, so their latencies
+  // overlap instead of adding up.
+  const int ctx_len = a.context_lens[seq];
+  const int blk_first = table[min((tile0 + wave) >> tpb_shift, a.max_blocks_per_seq - 1)];
+  const int blk_second = table[min((tile0 + wave + kWaves) >> tpb_shift, a.max_blocks_per_seq - 1)];
 
   // ---- shared query load --------------------------------------------------
   __shared__ uint4 q_lds[GT * CH];
@@ -78,6 +76,18 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
       q_lds[i] = (i < nh * CH) ? qg[i] : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
+
+  const int L = min(ctx_len, a.max_blocks_per_seq * BS);
+  if (L <= 0) {
+    if (single) {
+      uint4* o = reinterpret_cast<uint4*>(a.out) + ((size_t)seq * a.num_heads + h0) * CH;
+      for (int i = threadIdx.x; i < nh * CH; i += kWaves * 64) o[i] = make_uint4(0, 0, 0, 0);
+    }
+    return;
+  }
+  if (tok0 >= L) return;  // partition past this sequence's end: nothing to do
+  const int tok1 = min(L, tok0 + a.partition_blocks * BS);
+  const int ntiles = (tok1 - tok0 + TT - 1) / TT;
   uint32_t qv[GT][4];
   float slope[GT];
 #pragma unroll
@@ -97,7 +107,6 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
   }
 
   // ---- block walk -----------------------------------------------------------
-  const int* table = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
   using KS = KVStore<Fmt, KV8>;  // cache storage: 16-bit, or FP8 converted at use
   constexpr int ES = KS::kBytes;
   const size_t bstride = (size_t)a.kv_block_stride;  // bytes per physical block
@@ -196,8 +205,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
   int u = wave;
   if (u < ntiles) {
     VTile ta, tb2;
-    load(ta, u, block_of(u));
-    int blk_next = block_of(u + kWaves);
+    // the first two block ids were fetched with the query (a second tile
+    // past the partition reads nothing; its id is then the first one's)
+    load(ta, u, blk_first);
+    int blk_next = u + kWaves < ntiles ? blk_second : blk_first;
     while (true) {
       const int u1 = u + kWaves;
       load(tb2, u1, blk_next);
