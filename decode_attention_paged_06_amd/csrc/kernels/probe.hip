@@ -48,13 +48,6 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
 
 }  // namespace
 
-// One workgroup per 32 KB of the buffer, at most kStreamReadMaxBlocks.
-int stream_read_grid(size_t bytes) {
-  const size_t n16 = bytes / 16;
-  const size_t blocks = (n16 + 2047) / 2048;
-  return (int)(blocks < (size_t)kStreamReadMaxBlocks ? blocks : (size_t)kStreamReadMaxBlocks);
-}
-
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s) {
   const int grid = stream_read_grid(bytes);
   if (grid == 0) return hipSuccess;

@@ -102,7 +102,11 @@ hipError_t launch_cache_write(void* k_cache, void* v_cache, const void* k_new, c
 // `sink` holds stream_read_grid(bytes) 16-byte slots (practically never
 // written).  At most kStreamReadMaxBlocks workgroups of 256 threads.
 constexpr int kStreamReadMaxBlocks = 4096;
-int stream_read_grid(size_t bytes);
+// One workgroup per 32 KB of the buffer, at most kStreamReadMaxBlocks.
+inline int stream_read_grid(size_t bytes) {
+  const size_t blocks = (bytes / 16 + 2047) / 2048;
+  return (int)(blocks < (size_t)kStreamReadMaxBlocks ? blocks : (size_t)kStreamReadMaxBlocks);
+}
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 
 }  // namespace pa
