@@ -15,7 +15,7 @@ from decode_attention_paged_06_amd import (gather_cached_kv, joint_kv_cache, kv_
                                            paged_attention_prefill, paged_kv_cache_write)
 from decode_attention_paged_06_amd._lib import PA_KV_JOINT, PA_KV_SEPARATE
 from gpu_util import compare, device, make, oracle_ref, run, sample_seqs
-from workloads import gather_inputs, prefill_inputs, raw_bits, raw_u16, workload_args
+from workloads import WORKLOADS, gather_inputs, prefill_inputs, raw_bits, raw_u16, workload_args
 
 pytestmark = pytest.mark.gpu
 
@@ -71,10 +71,14 @@ def test_decode_joint_layout(case):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{what}: differs from separate"
 
 
-@pytest.mark.parametrize("name,batch,kv", [("gqa_ctx4096", 256, None), ("gqa_ctx4096", 256, "fp8"),
-                                           ("mqa_ragged_alibi", 256, None)])
+BENCH_CASES = ([(name, b, None) for name, w in WORKLOADS.items() for b in w["batches"]]
+               + [("gqa_ctx4096", 256, "fp8"), ("gqa_ctx4096", 16, "fp8"), ("mqa_ragged_alibi", 256, "fp8")])
+
+
+@pytest.mark.parametrize("name,batch,kv", BENCH_CASES, ids=[f"{n}-b{b}-{k or 'native'}" for n, b, k in BENCH_CASES])
 def test_bench_shapes_joint_layout(name, batch, kv):
-    """The bench's workloads in the joint layout at full size, auto plan (sampled rows)."""
+    """Every bench workload in the joint layout (the bench's default) at full size, in the
+    auto launch configuration the bench times (rows sampled beyond 16 sequences)."""
     args = workload_args(name, batch)
     if kv:
         args["kv_dtype"] = kv
