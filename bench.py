@@ -261,12 +261,13 @@ def calibrate_copy(mib, steps):
                       "bytes_written_per_copy": n, "copies": steps}), flush=True)
 
 
-def device_ceiling(gib: int = 4, reps: int = 10):
-    """What plain device-wide streaming reaches on this GPU, as context for the
-    kernel's fraction of the vendor peak: the library's streaming-read probe
-    over `gib` GiB (the decode kernels' 16-byte non-temporal loads, contiguous
-    runs, reads only) and a device-to-device copy of 1 GiB (the runtime's copy
-    kernel, read and written)."""
+def device_ceiling(gib: int = 4, reps: int = 10, run_bytes: int = 8192):
+    """What plain device-wide reading reaches on this GPU, as context for the
+    kernel's fraction of the vendor peak: the library's read probe over `gib`
+    GiB (the decode kernels' 16-byte non-temporal loads, reads only) in
+    contiguous slices and as `run_bytes` runs at scattered positions (the
+    paged pattern: one run per cache tile), and a device-to-device copy of
+    1 GiB (the runtime's copy kernel, read and written)."""
     import torch
 
     from decode_attention_paged_06_amd.ops import stream_read_probe
@@ -275,9 +276,10 @@ def device_ceiling(gib: int = 4, reps: int = 10):
     big = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
     sink = stream_read_probe(big)
     src, dst = big[: 1 << 30], torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for _ in range(2):
         stream_read_probe(big, sink)
+        stream_read_probe(big, sink, run_bytes=run_bytes)
         dst.copy_(src)
     torch.cuda.synchronize()
     e[0].record()
@@ -286,21 +288,29 @@ def device_ceiling(gib: int = 4, reps: int = 10):
     e[1].record()
     e[2].record()
     for _ in range(reps):
-        dst.copy_(src)
+        stream_read_probe(big, sink, run_bytes=run_bytes)
     e[3].record()
+    e[4].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e[5].record()
     torch.cuda.synchronize()
     read_s = e[0].elapsed_time(e[1]) * 1e-3 / reps
-    copy_s = e[2].elapsed_time(e[3]) * 1e-3 / reps
+    runs_s = e[2].elapsed_time(e[3]) * 1e-3 / reps
+    copy_s = e[4].elapsed_time(e[5]) * 1e-3 / reps
     del big, sink, src, dst
     torch.cuda.empty_cache()
     read_gbps = n / read_s / 1e9
+    runs_gbps = n / runs_s / 1e9
     copy_gbps = 2 * (1 << 30) / copy_s / 1e9
     return {"stream_read_GB/s": round(read_gbps, 1),
             "stream_read_pct_of_peak": round(100 * read_gbps / HBM_PEAK_GBPS, 1),
+            f"scattered_{run_bytes // 1024}KiB_runs_read_GB/s": round(runs_gbps, 1),
+            f"scattered_{run_bytes // 1024}KiB_runs_read_pct_of_peak": round(100 * runs_gbps / HBM_PEAK_GBPS, 1),
             "copy_GB/s_read_plus_write": round(copy_gbps, 1),
             "copy_pct_of_peak": round(100 * copy_gbps / HBM_PEAK_GBPS, 1),
-            "note": f"streaming-read probe over {gib} GiB and torch copy_ of 1 GiB, {reps} each, "
-                    f"after the timed region"}
+            "note": f"read probe over {gib} GiB (contiguous slices; {run_bytes} B runs at scattered "
+                    f"positions) and torch copy_ of 1 GiB, {reps} each, after the timed region"}
 
 
 PROFILE_DIR = os.path.join(ROOT, "profiles")

@@ -86,7 +86,7 @@ def lib() -> ctypes.CDLL:
     L.gather_cached_kv.restype = ctypes.c_int
     L.paged_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     L.paged_kv_cache_write.restype = ctypes.c_int
-    L.pa_stream_read_probe.argtypes = [vp, sz, vp, sz, vp]
+    L.pa_stream_read_probe.argtypes = [vp, sz, sz, vp, sz, vp]
     L.pa_stream_read_probe.restype = ctypes.c_int
     L.pa_stream_read_sink_bytes.argtypes = [sz]
     L.pa_stream_read_sink_bytes.restype = sz

@@ -539,9 +539,14 @@ int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
 
 size_t pa_stream_read_sink_bytes(size_t bytes) { return (size_t)pa::stream_read_grid(bytes) * 16; }
 
-int pa_stream_read_probe(const void* src, size_t bytes, void* sink, size_t sink_bytes,
-                         pa_stream_t stream) {
+int pa_stream_read_probe(const void* src, size_t bytes, size_t run_bytes, void* sink,
+                         size_t sink_bytes, pa_stream_t stream) {
+  auto pow2 = [](size_t x) { return x != 0 && (x & (x - 1)) == 0; };
   if (bytes % 16 != 0) return fail(PA_ERR_INVALID_ARG, "bytes %zu is not a multiple of 16", bytes);
+  if (run_bytes != 0 && (!pow2(run_bytes) || run_bytes < 1024 || bytes % run_bytes != 0 ||
+                         !pow2(bytes / run_bytes)))
+    return fail(PA_ERR_INVALID_ARG,
+                "run_bytes %zu: a power of two >= 1024 with bytes / run_bytes a power of two", run_bytes);
   if (bytes == 0) return ok();
   if (!src || !sink) return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(src, 16) || !aligned(sink, 16))
@@ -549,7 +554,8 @@ int pa_stream_read_probe(const void* src, size_t bytes, void* sink, size_t sink_
   if (sink_bytes < pa_stream_read_sink_bytes(bytes))
     return fail(PA_ERR_INVALID_ARG, "sink needs %zu bytes, got %zu", pa_stream_read_sink_bytes(bytes),
                 sink_bytes);
-  const hipError_t e = pa::launch_stream_read(src, bytes, sink, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e =
+      pa::launch_stream_read(src, bytes, run_bytes, sink, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "probe launch: %s", hipGetErrorString(e));
   return ok();
 }

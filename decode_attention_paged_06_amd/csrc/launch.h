@@ -107,6 +107,10 @@ inline int stream_read_grid(size_t bytes) {
   const size_t blocks = (bytes / 16 + 2047) / 2048;
   return (int)(blocks < (size_t)kStreamReadMaxBlocks ? blocks : (size_t)kStreamReadMaxBlocks);
 }
-hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
+// run_bytes: 0 for contiguous slices per workgroup, else runs of run_bytes (a
+// power of two >= 1024 dividing bytes, bytes / run_bytes a power of two) at
+// scattered positions.
+hipError_t launch_stream_read(const void* src, size_t bytes, size_t run_bytes, void* sink,
+                              hipStream_t s);
 
 }  // namespace pa

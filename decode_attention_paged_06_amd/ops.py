@@ -221,16 +221,18 @@ def paged_kv_cache_write(key_cache: torch.Tensor, value_cache: torch.Tensor, key
     return key_cache, value_cache
 
 
-def stream_read_probe(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None):
-    """Enqueue one streaming read of ``src``'s bytes (a measurement aid; see
-    pa_stream_read_probe).  Returns the sink tensor (allocated when omitted)."""
+def stream_read_probe(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None,
+                      run_bytes: int = 0):
+    """Enqueue one read of ``src``'s bytes (a measurement aid; see
+    pa_stream_read_probe): contiguous slices, or runs of ``run_bytes`` at
+    scattered positions.  Returns the sink tensor (allocated when omitted)."""
     _require(src, "src")
     nbytes = src.numel() * src.element_size()
     need = int(lib().pa_stream_read_sink_bytes(nbytes))
     if sink is None:
         sink = torch.empty(max(need, 16), dtype=torch.uint8, device=src.device)
     _require(sink, "sink")
-    check(lib().pa_stream_read_probe(src.data_ptr(), nbytes, sink.data_ptr(),
+    check(lib().pa_stream_read_probe(src.data_ptr(), nbytes, int(run_bytes), sink.data_ptr(),
                                      sink.numel() * sink.element_size(), _stream_ptr(stream)))
     return sink
 

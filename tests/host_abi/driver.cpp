@@ -192,9 +192,13 @@ static void probe() {
   g_launches.clear();
   const size_t n = size_t(4) << 30;
   CHECK(pa_stream_read_sink_bytes(n) == 16 * 4096);
-  CHECK(pa_stream_read_probe(FAKE, n, FAKE, 16 * 4096, nullptr) == PA_OK);
-  CHECK(g_launches.size() == 1 && g_launches[0].bytes == n);
-  CHECK(pa_stream_read_probe(FAKE, n, FAKE, 16, nullptr) == PA_ERR_INVALID_ARG);
+  CHECK(pa_stream_read_probe(FAKE, n, 0, FAKE, 16 * 4096, nullptr) == PA_OK);
+  CHECK(pa_stream_read_probe(FAKE, n, 8192, FAKE, 16 * 4096, nullptr) == PA_OK);
+  CHECK(g_launches.size() == 2 && g_launches[0].bytes == n && g_launches[1].run_bytes == 8192);
+  CHECK(pa_stream_read_probe(FAKE, n, 0, FAKE, 16, nullptr) == PA_ERR_INVALID_ARG);
+  CHECK(pa_stream_read_probe(FAKE, n, 512, FAKE, 16 * 4096, nullptr) == PA_ERR_INVALID_ARG);   // below 1 KB
+  CHECK(pa_stream_read_probe(FAKE, n, 3072, FAKE, 16 * 4096, nullptr) == PA_ERR_INVALID_ARG);  // not 2^k
+  CHECK(pa_stream_read_probe(FAKE, 3 * 8192, 8192, FAKE, 16 * 4096, nullptr) == PA_ERR_INVALID_ARG);
 }
 
 static void last_error_is_per_thread() {

@@ -77,9 +77,10 @@ hipError_t launch_cache_write(void*, void*, const void*, const void*, const int3
   l.head_stride = head_stride;
   return hipSuccess;
 }
-hipError_t launch_stream_read(const void*, size_t bytes, void*, hipStream_t) {
+hipError_t launch_stream_read(const void*, size_t bytes, size_t run_bytes, void*, hipStream_t) {
   record("probe", nullptr, 0, 0, false);
   g_launches.back().bytes = bytes;
+  g_launches.back().run_bytes = run_bytes;
   return hipSuccess;
 }
 }  // namespace pa

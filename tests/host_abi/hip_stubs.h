@@ -17,7 +17,7 @@ struct Launch {
   const void* ptr;
   int32_t num_tokens, num_kv_heads, row_bytes, block_size;
   int64_t block_stride, head_stride;
-  size_t bytes;
+  size_t bytes, run_bytes;
 };
 
 extern std::vector<Launch> g_launches;

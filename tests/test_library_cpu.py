@@ -387,8 +387,10 @@ def test_stream_read_probe_validation(L):
     assert L.pa_stream_read_sink_bytes(0) == 0
     assert L.pa_stream_read_sink_bytes(16 * 2048) == 16            # one workgroup per 32 KB
     assert L.pa_stream_read_sink_bytes(1 << 32) == 16 * 4096      # grid capped at 4096 workgroups
-    assert p(FAKE, 24, FAKE, 1 << 20, None) == INVALID              # not a multiple of 16
-    assert p(None, 1024, FAKE, 1 << 20, None) == INVALID
-    assert p(FAKE + 8, 1024, FAKE, 1 << 20, None) == ALIGN
-    assert p(FAKE, 1 << 20, FAKE, 16, None) == INVALID              # sink too small
-    assert p(None, 0, None, 0, None) == OK
+    assert p(FAKE, 24, 0, FAKE, 1 << 20, None) == INVALID           # not a multiple of 16
+    assert p(None, 1024, 0, FAKE, 1 << 20, None) == INVALID
+    assert p(FAKE + 8, 1024, 0, FAKE, 1 << 20, None) == ALIGN
+    assert p(FAKE, 1 << 20, 0, FAKE, 16, None) == INVALID           # sink too small
+    assert p(FAKE, 1 << 20, 1000, FAKE, 1 << 20, None) == INVALID   # runs: powers of two >= 1 KB
+    assert p(FAKE, 3 << 13, 1 << 13, FAKE, 1 << 20, None) == INVALID  # run count not a power of two
+    assert p(None, 0, 0, None, 0, None) == OK
