@@ -22,10 +22,19 @@ def make(device_="cpu", **kw):
 
 
 def to_device(inp, dev):
-    for k in ("query", "key_cache", "value_cache", "block_tables", "context_lens", "alibi_slopes"):
-        t = getattr(inp, k)
+    """Move a batch to `dev`, keeping joint K/V caches joint (one tensor, two views)."""
+    k, v = inp.key_cache, inp.value_cache
+    if not (k.is_contiguous() and v.is_contiguous()):
+        NB, Hkv, BS, D = k.shape
+        assert v.data_ptr() == k.data_ptr() + BS * D * k.element_size(), "not a joint cache"
+        kv = torch.as_strided(k, (NB, Hkv, 2, BS, D), (2 * Hkv * BS * D, 2 * BS * D, BS * D, D, 1)).to(dev)
+        inp.key_cache, inp.value_cache = kv[:, :, 0], kv[:, :, 1]
+    else:
+        inp.key_cache, inp.value_cache = k.to(dev), v.to(dev)
+    for name in ("query", "block_tables", "context_lens", "alibi_slopes"):
+        t = getattr(inp, name)
         if t is not None:
-            setattr(inp, k, t.to(dev))
+            setattr(inp, name, t.to(dev))
     return inp
 
 

@@ -2,8 +2,8 @@
 
 The targeted tests fix one or two parameters at a time; these draw whole
 configurations at random (group size, head size, dtype, block size, cache
-format, ALiBi, engine, partition size, schedule, ragged lengths, and new-token
-counts for the multi-query call) from a fixed seed, so combinations nobody
+format and layout, ALiBi, engine, partition size, schedule, ragged lengths, and
+new-token counts for the multi-query call) from a fixed seed, so combinations nobody
 wrote down are checked against the fp64 oracle too.  Sizes stay small enough
 for the oracle to finish in seconds.
 """
@@ -33,10 +33,11 @@ def draw_decode(rng):
                 alibi=bool(rng.integers(0, 2)), fp8=bool(rng.integers(0, 4) == 0),
                 engine=str(rng.choice(["auto", "valu", "mfma"])),
                 ps=int(rng.choice([-1, 0, 0, 128, 256, 512])),
-                schedule=str(rng.choice(["auto", "grid", "longest_first"])))
+                schedule=str(rng.choice(["auto", "grid", "longest_first"])),
+                layout=str(rng.choice(["separate", "joint"])))
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_decode(seed):
     dev = device()
     c = draw_decode(np.random.default_rng(1000 + seed))
@@ -44,13 +45,13 @@ def test_random_decode(seed):
     inp = to_device(make(num_seqs=len(c["lens"]), num_heads=c["G"] * c["Hkv"],
                          num_kv_heads=c["Hkv"], head_size=c["D"], block_size=c["BS"],
                          dtype=c["dtype"], seed=seed, context_lens=c["lens"], alibi=c["alibi"],
-                         poison=True, kv_dtype="fp8" if c["fp8"] else None), dev)
+                         poison=True, kv_dtype="fp8" if c["fp8"] else None, kv_layout=c["layout"]), dev)
     ref = oracle_ref(inp)
     out = run(inp, engine=c["engine"], partition_size=ps, schedule=c["schedule"])
     compare(out, ref, c["dtype"], what=f"seed {seed}: {c}")
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_prefill(seed):
     dev = device()
     rng = np.random.default_rng(2000 + seed)
@@ -66,13 +67,14 @@ def test_random_prefill(seed):
         news[0] = 1
     alibi = bool(rng.integers(0, 2))
     fp8 = bool(rng.integers(0, 4) == 0)
+    ps = int(rng.choice([-1, 0, max(BS, 64)]))
+    layout = str(rng.choice(["separate", "joint"]))
     inp, q, qs, max_q = prefill_inputs(new_tokens=news, seed=seed, device=dev, num_seqs=S,
                                        num_heads=G * Hkv, num_kv_heads=Hkv, head_size=D,
                                        block_size=BS, dtype=dtype, context_lens=lens,
                                        alibi=alibi, poison=True,
-                                       kv_dtype="fp8" if fp8 else None)
+                                       kv_dtype="fp8" if fp8 else None, kv_layout=layout)
     ref = ref_prefill(inp, q, qs)
-    ps = int(rng.choice([-1, 0, max(BS, 64)]))
     compare(run_prefill(inp, q, qs, max_q, ps), ref, dtype,
             what=f"seed {seed}: G={G} Hkv={Hkv} D={D} {dtype} BS={BS} lens={lens} new={news} "
-                 f"alibi={alibi} fp8={fp8} partition={ps}")
+                 f"alibi={alibi} fp8={fp8} partition={ps} layout={layout}")
