@@ -407,7 +407,7 @@ def cpu_baseline(args, budget_s):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); the decode "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {a.gpus}); the decode "
               "kernel has no cross-GPU path to measure", file=sys.stderr)
         sys.exit(2)
     if a.calibrate_copy:
