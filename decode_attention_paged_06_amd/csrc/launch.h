@@ -19,8 +19,8 @@ constexpr int kMaxGroup = 64;    // largest num_heads / num_kv_heads supported
 struct DecodeArgs {
   void* out;                    // [S, Hq, D] storage type
   const void* q;                // [S, Hq, D]
-  const void* k_cache;          // [NB, Hkv, BS, D]
-  const void* v_cache;          // [NB, Hkv, BS, D]
+  const void* k_cache;          // first K tile; (block, kv head) tiles of [BS, D] at the strides below
+  const void* v_cache;          // first V tile; same strides
   const int32_t* block_tables;  // [S, MAXB]
   const int32_t* context_lens;  // [S]
   const float* alibi;           // [Hq] or nullptr
