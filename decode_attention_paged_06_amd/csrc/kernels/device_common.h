@@ -208,13 +208,37 @@ struct LdsPiece {
   }
 };
 
-// Bytes 0 .. BYTES - 1 of the buffer to dst (BYTES a multiple of 1 KB; one
-// transfer per KB).
+// Bytes 0 .. BYTES - 1 of the buffer to dst (BYTES 1, 2 or 4 KB; one transfer
+// per KB).  The run is contiguous at both ends, so one M0 set-up serves all its
+// transfers: the instruction's immediate offset advances the memory and the
+// LDS address alike (measured: FP8 MQA 111.5 -> 109.1 us, prefill 611 -> 621
+// TFLOP/s against an M0 set-up per transfer).
 template <int BYTES>
 __device__ __forceinline__ void lds_copy_run(rsrc_t r, char* dst, int lane) {
-  static_assert(BYTES % 1024 == 0, "whole transfers");
-#pragma unroll
-  for (int c = 0; c < BYTES / 1024; ++c) lds_load16(r, 1024u * c + 16u * lane, dst + 1024 * c);
+  static_assert(BYTES == 1024 || BYTES == 2048 || BYTES == 4096, "1, 2 or 4 transfers");
+  const uint32_t off = 16u * lane;
+  uint32_t saved;
+  if constexpr (BYTES == 4096) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %3, 0 offen offset:0 nt lds\n\t"
+        "buffer_load_dwordx4 %1, %3, 0 offen offset:1024 nt lds\n\t"
+        "buffer_load_dwordx4 %1, %3, 0 offen offset:2048 nt lds\n\t"
+        "buffer_load_dwordx4 %1, %3, 0 offen offset:3072 nt lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(lds_address(dst)), "s"(r)
+        : "memory");
+  } else if constexpr (BYTES == 2048) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %3, 0 offen offset:0 nt lds\n\t"
+        "buffer_load_dwordx4 %1, %3, 0 offen offset:1024 nt lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(lds_address(dst)), "s"(r)
+        : "memory");
+  } else {
+    lds_load16(r, off, dst);
+  }
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
