@@ -533,7 +533,13 @@ def main():
         torch.cuda.synchronize()
         graph_us = g0.elapsed_time(g1) * 1e3 / (reps * ncap)
 
-    ceiling = None if a.no_ceiling else device_ceiling()
+    ceiling = None
+    if not a.no_ceiling:
+        try:
+            ceiling = device_ceiling()
+        except torch.cuda.OutOfMemoryError as e:  # context only: never fail the bench for it
+            ceiling = {"error": f"not measured: {e.__class__.__name__}"}
+            torch.cuda.empty_cache()
 
     kernel_name = "decode_mfma_kernel" if plan.engine == 2 else "decode_valu_kernel"
     context = PAGES_US.get((name, batch))
