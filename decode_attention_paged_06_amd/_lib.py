@@ -23,7 +23,9 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_E
 EXPORTS = ("paged_attention_decode", "paged_attention_workspace_bytes", "paged_attention_plan",
            "paged_attention_prefill", "paged_attention_prefill_workspace_bytes",
            "paged_attention_prefill_plan", "gather_cached_kv", "paged_kv_cache_write",
-           "pa_status_string", "pa_last_error", "pa_stream_read_probe", "pa_stream_read_sink_bytes")
+           "pa_status_string", "pa_last_error")
+# The measurement aid of csrc/measure.h (exported, not part of the public header).
+MEASURE_EXPORTS = ("pa_stream_read_probe", "pa_stream_read_sink_bytes")
 
 
 class PaDims(ctypes.Structure):

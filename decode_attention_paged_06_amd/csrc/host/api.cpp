@@ -11,6 +11,7 @@
 #include <cstring>
 
 #include "launch.h"
+#include "measure.h"
 
 namespace {
 

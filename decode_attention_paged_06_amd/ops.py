@@ -81,6 +81,66 @@ def _require(t: torch.Tensor, name: str, dtype=None, dense: bool = True):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _shape_error(msg: str):
+    raise ValueError(msg)
+
+
+def _check_attention_shapes(out, query, key_cache, value_cache, block_tables, context_lens,
+                            alibi_slopes, num_seqs: int, query_start_loc=None):
+    """Shapes the C layer cannot see (it gets pointers): every tensor must
+    match the query and the caches, or the kernels would read or write past
+    an allocation."""
+    if query.dim() != 3:
+        _shape_error(f"query must be [tokens, num_heads, head_size], got {tuple(query.shape)}")
+    if tuple(out.shape) != tuple(query.shape):
+        _shape_error(f"out {tuple(out.shape)} must have the query's shape {tuple(query.shape)}")
+    if key_cache.dim() != 4 or tuple(key_cache.shape) != tuple(value_cache.shape):
+        _shape_error("key_cache and value_cache must both be [num_blocks, num_kv_heads, block_size, "
+                     f"head_size], got {tuple(key_cache.shape)} and {tuple(value_cache.shape)}")
+    if key_cache.shape[3] != query.shape[2]:
+        _shape_error(f"cache head_size {key_cache.shape[3]} differs from the query's {query.shape[2]}")
+    if block_tables.dim() != 2 or block_tables.shape[0] < num_seqs:
+        _shape_error(f"block_tables must be [num_seqs, max_blocks_per_seq] with at least {num_seqs} "
+                     f"rows, got {tuple(block_tables.shape)}")
+    if context_lens.dim() != 1 or context_lens.shape[0] != num_seqs:
+        _shape_error(f"context_lens must hold {num_seqs} entries, got {tuple(context_lens.shape)}")
+    if alibi_slopes is not None and (alibi_slopes.dim() != 1 or
+                                     alibi_slopes.shape[0] != query.shape[1]):
+        _shape_error(f"alibi_slopes must hold one slope per query head ({query.shape[1]}), got "
+                     f"{tuple(alibi_slopes.shape)}")
+    if query_start_loc is not None and (query_start_loc.dim() != 1 or
+                                        query_start_loc.shape[0] != num_seqs + 1):
+        _shape_error(f"query_start_loc must hold num_seqs + 1 = {num_seqs + 1} entries, got "
+                     f"{tuple(query_start_loc.shape)}")
+
+
+def _check_row_copy_shapes(rows_k, rows_v, key_cache, value_cache, slot_mapping):
+    """[T, Hkv, D] row arrays against the caches and the slot list."""
+    if key_cache.dim() != 4 or tuple(key_cache.shape) != tuple(value_cache.shape):
+        _shape_error("key_cache and value_cache must both be [num_blocks, num_kv_heads, block_size, "
+                     f"head_size], got {tuple(key_cache.shape)} and {tuple(value_cache.shape)}")
+    if slot_mapping.dim() != 1:
+        _shape_error(f"slot_mapping must be 1-D, got {tuple(slot_mapping.shape)}")
+    want = (slot_mapping.shape[0], key_cache.shape[1], key_cache.shape[3])
+    for t, n in ((rows_k, "key rows"), (rows_v, "value rows")):
+        if tuple(t.shape) != want:
+            _shape_error(f"{n} must be [num_tokens, num_kv_heads, head_size] = {want}, got "
+                         f"{tuple(t.shape)}")
+
+
+def _owned_workspace(nbytes: int, device, stream):
+    """A temporary workspace for one call.  The kernels run on `stream`; when
+    that is not torch's current stream the allocation is recorded on it, so
+    the caching allocator does not hand the memory to other work before the
+    call's kernels on `stream` are done with it."""
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ptr = _stream_ptr(stream)
+    if ptr != torch.cuda.current_stream(device).cuda_stream:
+        ws.record_stream(stream if isinstance(stream, torch.cuda.Stream)
+                         else torch.cuda.ExternalStream(ptr, device=device))
+    return ws
+
+
 def paged_attention_plan(dims: PaDims, workspace_bytes: int, opts: Optional[PaOpts] = None) -> PaPlan:
     plan = PaPlan()
     check(lib().paged_attention_plan(ctypes.byref(dims), workspace_bytes,
@@ -106,6 +166,8 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
     code * k_scale / code * v_scale.  ``workspace`` (uint8 device tensor) is
     allocated with torch when omitted and the plan needs one.
     """
+    _check_attention_shapes(out, query, key_cache, value_cache, block_tables, context_lens,
+                            alibi_slopes, query.shape[0] if query.dim() == 3 else 0)
     _require(out, "out", query.dtype)
     _require(query, "query", query.dtype)
     kv_dtype = torch.float8_e4m3fn if key_cache.dtype == torch.float8_e4m3fn else query.dtype
@@ -123,7 +185,7 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
     if workspace is None:
         nbytes = paged_attention_workspace_bytes(dims, opts)
         if nbytes:
-            workspace = torch.empty(nbytes, dtype=torch.uint8, device=query.device)
+            workspace = _owned_workspace(nbytes, query.device, stream)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         _require(workspace, "workspace")
@@ -152,6 +214,9 @@ def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: t
                             workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
                             k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
     """Enqueue causal multi-query attention for packed new tokens; returns ``out``."""
+    _check_attention_shapes(out, query, key_cache, value_cache, block_tables, context_lens,
+                            alibi_slopes, context_lens.shape[0] if context_lens.dim() == 1 else -1,
+                            query_start_loc)
     _require(out, "out", query.dtype)
     _require(query, "query", query.dtype)
     kv_dtype = torch.float8_e4m3fn if key_cache.dtype == torch.float8_e4m3fn else query.dtype
@@ -171,7 +236,7 @@ def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: t
         nbytes = int(lib().paged_attention_prefill_workspace_bytes(
             ctypes.byref(dims), T, int(max_query_len), ctypes.byref(opts)))
         if nbytes:
-            workspace = torch.empty(nbytes, dtype=torch.uint8, device=query.device)
+            workspace = _owned_workspace(nbytes, query.device, stream)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         _require(workspace, "workspace")
@@ -189,6 +254,7 @@ def gather_cached_kv(key_out: torch.Tensor, value_out: torch.Tensor, key_cache: 
                      value_cache: torch.Tensor, slot_mapping: torch.Tensor, block_size: int,
                      stream=None):
     """Enqueue the bit-exact gather of cache rows into key_out/value_out ([T, Hkv, D])."""
+    _check_row_copy_shapes(key_out, value_out, key_cache, value_cache, slot_mapping)
     for t, n in ((key_out, "key_out"), (value_out, "value_out")):
         _require(t, n, key_cache.dtype)
     for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
@@ -207,6 +273,7 @@ def paged_kv_cache_write(key_cache: torch.Tensor, value_cache: torch.Tensor, key
                          value: torch.Tensor, slot_mapping: torch.Tensor, block_size: int,
                          stream=None):
     """Enqueue the bit-exact store of key/value rows ([T, Hkv, D]) into their cache slots."""
+    _check_row_copy_shapes(key, value, key_cache, value_cache, slot_mapping)
     for t, n in ((key, "key"), (value, "value")):
         _require(t, n, key_cache.dtype)
     for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):

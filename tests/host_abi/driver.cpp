@@ -10,6 +10,7 @@
 
 #include "hip_stubs.h"
 #include "paged_attention.h"
+#include "measure.h"
 
 static int g_fail = 0;
 #define CHECK(c)                                                                 \

@@ -1,8 +1,9 @@
 """GPU parity: the HIP decode path against the fp64 oracle.
 
-Tolerance (max abs, per element): 2e-3 for fp16, 1e-2 for bf16.  Integer
-facts (context length 1 returns V, relabelled blocks, determinism) are
-checked bit for bit.
+The gate (tests/parity_gate.py): max abs per element 2e-3 for fp16, 1e-2 for
+bf16, plus relative L2 bounds over the whole output (2 u) and per output row
+(4 u), u the output format's unit roundoff.  Integer facts (context length 1
+returns V, relabelled blocks, determinism) are checked bit for bit.
 """
 import numpy as np
 import pytest
@@ -215,6 +216,31 @@ def test_stream_argument_is_used():
                                inp.context_lens, inp.scale, 16, None, stream=s, partition_size=64)
     s.synchronize()
     compare(out, ref, "bf16", what="side stream")
+
+
+def test_side_stream_without_context_manager_owns_its_workspace():
+    """stream=s while torch's current stream is another one, workspace=None:
+    the binding's temporary workspace is recorded on s, so the allocator does
+    not hand it to work on the current stream while the kernels on s run."""
+    dev = device()
+    inp = to_device(make(num_seqs=2, num_heads=64, num_kv_heads=8, head_size=128, block_size=16,
+                         dtype="bf16", seed=42, context_lens=[4000, 3000]), dev)
+    ref = oracle_ref(inp)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    from decode_attention_paged_06_amd import paged_attention_decode
+    outs = []
+    for _ in range(8):
+        out = torch.empty_like(inp.query)
+        paged_attention_decode(out, inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
+                               inp.context_lens, inp.scale, 16, None, stream=s, partition_size=128)
+        # work on the current stream that would reuse a freed block at once
+        junk = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+        junk.fill_(0xFF)
+        outs.append(out)
+    s.synchronize()
+    for k, out in enumerate(outs):
+        compare(out, ref, "bf16", what=f"side stream call {k}, binding-allocated workspace")
 
 
 def test_concurrent_streams():

@@ -16,6 +16,7 @@ from decode_attention_paged_06_amd._lib import PaDims, PaOpts, PaPlan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "paged_attention.h")
+MEASURE_HEADER = os.path.join(ROOT, "decode_attention_paged_06_amd", "csrc", "measure.h")
 
 OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, 1, 2, 3, 4
 
@@ -25,8 +26,8 @@ def L():
     return _lib.lib()
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=None):
+    text = open(path or HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, re.M)))
 
@@ -40,6 +41,11 @@ def test_exports_every_declared_symbol(L):
     for name in declared:
         assert name in exported, name
         assert getattr(L, name) is not None
+    # the measurement aid lives in an internal header, exported for the bench only
+    internal = header_functions(MEASURE_HEADER)
+    assert set(internal) == set(_lib.MEASURE_EXPORTS), internal
+    for name in internal:
+        assert name in exported, name
 
 
 def test_product_package_does_not_load_the_oracle():
