@@ -16,11 +16,13 @@ PA_KV_NATIVE, PA_KV_FP8_E4M3 = 0, 1
 PA_KV_SEPARATE, PA_KV_JOINT = 0, 1
 PA_ENGINE_AUTO, PA_ENGINE_VALU, PA_ENGINE_MFMA = 0, 1, 2
 PA_SCHEDULE_AUTO, PA_SCHEDULE_GRID, PA_SCHEDULE_LONGEST_FIRST = 0, 1, 2
+# PA_NOALLOC_SCRATCH_BYTES of include/paged_attention.h
+NOALLOC_SCRATCH_BYTES = 32 << 20
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_ALIGNMENT",
           4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH", 6: "PA_ERR_DEVICE"}
 
 # Every symbol include/paged_attention.h declares.
-EXPORTS = ("paged_attention_decode", "paged_attention_workspace_bytes", "paged_attention_plan",
+EXPORTS = ("paged_attention_decode", "paged_attention_decode_noalloc", "paged_attention_workspace_bytes", "paged_attention_plan",
            "paged_attention_prefill", "paged_attention_prefill_workspace_bytes",
            "paged_attention_prefill_plan", "gather_cached_kv", "paged_kv_cache_write",
            "pa_status_string", "pa_last_error")
@@ -69,6 +71,9 @@ def lib() -> ctypes.CDLL:
     L.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, vp, vp,
                                          ctypes.POINTER(PaDims), vp, sz, ctypes.POINTER(PaOpts)]
     L.paged_attention_decode.restype = ctypes.c_int
+    L.paged_attention_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, vp,
+                                                 vp, ctypes.POINTER(PaDims), ctypes.POINTER(PaOpts)]
+    L.paged_attention_decode_noalloc.restype = ctypes.c_int
     L.paged_attention_workspace_bytes.argtypes = [ctypes.POINTER(PaDims), ctypes.POINTER(PaOpts)]
     L.paged_attention_workspace_bytes.restype = sz
     L.paged_attention_plan.argtypes = [ctypes.POINTER(PaDims), sz, ctypes.POINTER(PaOpts),

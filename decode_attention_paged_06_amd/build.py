@@ -27,6 +27,7 @@ SOURCES = [
     "kernels/reduce.hip",
     "kernels/gather.hip",
     "kernels/schedule.hip",
+    "kernels/scratch.hip",
     "kernels/probe.hip",
 ]
 

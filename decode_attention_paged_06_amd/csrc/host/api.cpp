@@ -422,6 +422,35 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
                        workspace, workspace_bytes, opts);
 }
 
+int paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, float scale, int32_t block_size,
+                                   const float* alibi_slopes, pa_stream_t stream,
+                                   const pa_dims* dims, const pa_opts* opts) {
+  if (dims == nullptr) return fail(PA_ERR_INVALID_ARG, "dims is NULL");
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->num_seqs == 0) return ok();
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_DEVICE, "hipGetDevice failed");
+  void* scratch = nullptr;
+  const hipError_t e = pa::noalloc_scratch(dev, &scratch);
+  if (e != hipSuccess)
+    return fail(PA_ERR_DEVICE, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+  st = run_attention(out, query, key_cache, value_cache, block_tables, context_lens, nullptr,
+                     decode_shape(dims), scale, block_size, alibi_slopes, stream, dims, scratch,
+                     PA_NOALLOC_SCRATCH_BYTES, opts);
+  if (st == PA_ERR_WORKSPACE) {
+    char detail[sizeof(g_last_error)];
+    std::memcpy(detail, g_last_error, sizeof(detail));
+    return fail(PA_ERR_WORKSPACE,
+                "the forced partition_size needs more than the %zu-byte scratch of the "
+                "allocation-free entry point (%s)",
+                (size_t)PA_NOALLOC_SCRATCH_BYTES, detail);
+  }
+  return st;
+}
+
 static CallShape prefill_shape(int32_t num_query_tokens, int32_t max_query_len) {
   CallShape c;
   c.multi = true;

@@ -98,6 +98,11 @@ hipError_t launch_cache_write(void* k_cache, void* v_cache, const void* k_new, c
                               int32_t row_bytes, int32_t block_size, int64_t block_stride,
                               int64_t head_stride, hipStream_t s);
 
+// Device address of the allocation-free entry point's scratch array on
+// `device`, which must be the current device (looked up once per device,
+// then cached).  The array holds PA_NOALLOC_SCRATCH_BYTES bytes.
+hipError_t noalloc_scratch(int device, void** ptr);
+
 // Streaming-read probe: reads `bytes` (a multiple of 16) at `src` once;
 // `sink` holds stream_read_grid(bytes) 16-byte slots (practically never
 // written).  At most kStreamReadMaxBlocks workgroups of 256 threads.

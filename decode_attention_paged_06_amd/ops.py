@@ -198,6 +198,40 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
     return out
 
 
+def paged_attention_decode_noalloc(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                                   value_cache: torch.Tensor, block_tables: torch.Tensor,
+                                   context_lens: torch.Tensor, scale: float, block_size: int,
+                                   alibi_slopes: Optional[torch.Tensor] = None, stream=None,
+                                   partition_size: int = 0, engine: str = "auto",
+                                   k_scale: float = 1.0, v_scale: float = 1.0,
+                                   schedule: str = "auto") -> torch.Tensor:
+    """paged_attention_decode without a workspace: the split partials go to the
+    library's per-GPU scratch (see paged_attention_decode_noalloc in the C
+    header; calls that overlap on one GPU race).  Allocates nothing."""
+    _check_attention_shapes(out, query, key_cache, value_cache, block_tables, context_lens,
+                            alibi_slopes, query.shape[0] if query.dim() == 3 else 0)
+    _require(out, "out", query.dtype)
+    _require(query, "query", query.dtype)
+    kv_dtype = torch.float8_e4m3fn if key_cache.dtype == torch.float8_e4m3fn else query.dtype
+    _require(key_cache, "key_cache", kv_dtype, dense=False)
+    _require(value_cache, "value_cache", kv_dtype, dense=False)
+    layout = kv_layout_of(key_cache, value_cache)
+    _require(block_tables, "block_tables", torch.int32)
+    _require(context_lens, "context_lens", torch.int32)
+    if alibi_slopes is not None:
+        _require(alibi_slopes, "alibi_slopes", torch.float32)
+    if query.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {query.dtype}")
+    dims = make_dims(query, key_cache, block_tables, k_scale, v_scale, layout)
+    opts = make_opts(partition_size, engine, schedule=schedule)
+    check(lib().paged_attention_decode_noalloc(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), int(block_size),
+        alibi_slopes.data_ptr() if alibi_slopes is not None else None, _stream_ptr(stream),
+        ctypes.byref(dims), ctypes.byref(opts)))
+    return out
+
+
 def make_prefill_dims(query: torch.Tensor, key_cache: torch.Tensor, block_tables: torch.Tensor,
                       num_seqs: int, k_scale: float = 1.0, v_scale: float = 1.0,
                       kv_layout: int = PA_KV_SEPARATE) -> PaDims:
@@ -304,6 +338,6 @@ def stream_read_probe(src: torch.Tensor, sink: Optional[torch.Tensor] = None, st
     return sink
 
 
-__all__ = ["paged_attention_decode", "paged_attention_plan", "paged_attention_workspace_bytes",
+__all__ = ["paged_attention_decode", "paged_attention_decode_noalloc", "paged_attention_plan", "paged_attention_workspace_bytes",
            "paged_attention_prefill", "make_prefill_dims", "gather_cached_kv", "paged_kv_cache_write",
            "make_dims", "make_opts", "joint_kv_cache", "kv_layout_of", "stream_read_probe", "_lib"]

@@ -190,6 +190,35 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
                            void* workspace, size_t workspace_bytes, const pa_opts* opts);
 
 /*
+ * paged_attention_decode_noalloc -- paged_attention_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the split-context partials live
+ * in a scratch array the library itself holds on each GPU, so the caller
+ * passes only inputs and outputs.  Same kernels, same results (bit for bit)
+ * as paged_attention_decode given an equally large workspace.
+ *
+ * Arguments as paged_attention_decode, without the workspace.  The scratch
+ * holds at most PA_NOALLOC_SCRATCH_BYTES bytes: with opts == NULL (or
+ * opts->partition_size == 0) the planner uses fewer partitions when a split
+ * would need more, down to a single pass; a forced partition_size whose
+ * partials exceed it returns PA_ERR_WORKSPACE.  The array is a static part of
+ * the library's device code: each GPU the library runs on holds one until the
+ * process ends, and the first call on a device looks up its address (with
+ * that device current).  The call allocates nothing and fills no memory.
+ *
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents: calls that overlap on one GPU (on different streams, or
+ * from several threads without ordering) race and may return wrong results.
+ * Calls ordered on one stream are safe.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, float scale, int32_t block_size,
+                                   const float* alibi_slopes, pa_stream_t stream,
+                                   const pa_dims* dims, const pa_opts* opts);
+
+/*
  * paged_attention_workspace_bytes -- workspace the planner's choice needs for
  * these shapes and overrides when given unlimited workspace (0 if it picks a
  * single pass).  Host only; returns 0 for invalid dims.

@@ -202,6 +202,49 @@ static void probe() {
   CHECK(pa_stream_read_probe(FAKE, 3 * 8192, 8192, FAKE, 16 * 4096, nullptr) == PA_ERR_INVALID_ARG);
 }
 
+// The allocation-free entry point: split partials in the library's scratch,
+// the same launches as a call given that much workspace; a forced partition
+// size too large for the scratch is rejected before anything is launched.
+static void decode_noalloc() {
+  const auto tab = reinterpret_cast<const int32_t*>(FAKE);
+  pa_dims d = dims(1, 64, 8);  // batch 1: a split plan
+  g_launches.clear();
+  CHECK(paged_attention_decode_noalloc(FAKE, FAKE, FAKE, FAKE + (1 << 30), tab, tab, 0.088f, 16,
+                                       nullptr, nullptr, &d, nullptr) == PA_OK);
+  CHECK(g_launches.size() == 2 && std::strcmp(g_launches[1].kind, "reduce") == 0);
+  const Launch split = g_launches[0];
+  CHECK(split.a.num_partitions > 1);
+  CHECK(split.a.ws_o == reinterpret_cast<float*>(0x7f0000000000ull));
+  g_launches.clear();
+  char* ws = reinterpret_cast<char*>(0x7f0000000000ull);
+  CHECK(decode(d, FAKE, FAKE + (1 << 30), ws, PA_NOALLOC_SCRATCH_BYTES) == PA_OK);
+  CHECK(g_launches.size() == 2 && g_launches[0].a.num_partitions == split.a.num_partitions &&
+        g_launches[0].a.partition_blocks == split.a.partition_blocks);
+  // planned for 1024 CUs the auto split would exceed the scratch: fewer
+  // partitions, still OK (for 256 CUs every auto plan fits: at most
+  // 512 units x 64 heads x 128 x 4 bytes of partials)
+  pa_dims big = dims(4, 64, 1, 128, 16, 1 << 20, 1 << 16);
+  pa_opts o = {0, 0, 1024, 0};
+  pa_plan unlimited, fits;
+  CHECK(paged_attention_plan(&big, (size_t)1 << 40, &o, &unlimited) == PA_OK);
+  CHECK(unlimited.workspace_bytes > PA_NOALLOC_SCRATCH_BYTES);
+  CHECK(paged_attention_plan(&big, PA_NOALLOC_SCRATCH_BYTES, &o, &fits) == PA_OK);
+  CHECK(fits.workspace_bytes <= PA_NOALLOC_SCRATCH_BYTES && fits.num_partitions < unlimited.num_partitions);
+  g_launches.clear();
+  CHECK(paged_attention_decode_noalloc(FAKE, FAKE, FAKE, FAKE + (1 << 30), tab, tab, 0.088f, 16,
+                                       nullptr, nullptr, &big, &o) == PA_OK);
+  CHECK(!g_launches.empty() && g_launches[0].a.num_partitions == fits.num_partitions);
+  // forced: 256-token partitions of a 2^20-token bound need 4 * 64 * 4096 * 128 * 4 bytes
+  pa_opts forced = {256, 0, 256, 0};
+  g_launches.clear();
+  CHECK(paged_attention_decode_noalloc(FAKE, FAKE, FAKE, FAKE + (1 << 30), tab, tab, 0.088f, 16,
+                                       nullptr, nullptr, &big, &forced) == PA_ERR_WORKSPACE);
+  CHECK(g_launches.empty());
+  CHECK(std::string(pa_last_error()).find("scratch") != std::string::npos);
+  CHECK(paged_attention_decode_noalloc(FAKE, FAKE, FAKE, FAKE + (1 << 30), tab, tab, 0.088f, 16,
+                                       nullptr, nullptr, nullptr, nullptr) == PA_ERR_INVALID_ARG);
+}
+
 static void last_error_is_per_thread() {
   pa_dims bad = dims(1, 60, 8);
   CHECK(decode(bad, FAKE, FAKE) == PA_ERR_INVALID_ARG);
@@ -226,6 +269,7 @@ int main() {
   prefill();
   row_copies();
   probe();
+  decode_noalloc();
   last_error_is_per_thread();
   if (g_fail) {
     std::fprintf(stderr, "%d check(s) failed\n", g_fail);

@@ -77,6 +77,11 @@ hipError_t launch_cache_write(void*, void*, const void*, const void*, const int3
   l.head_stride = head_stride;
   return hipSuccess;
 }
+// A fake device address for the allocation-free entry point's scratch.
+hipError_t noalloc_scratch(int, void** ptr) {
+  *ptr = reinterpret_cast<void*>(uintptr_t(0x7f0000000000ull));
+  return hipSuccess;
+}
 hipError_t launch_stream_read(const void*, size_t bytes, size_t run_bytes, void*, hipStream_t) {
   record("probe", nullptr, 0, 0, false);
   g_launches.back().bytes = bytes;

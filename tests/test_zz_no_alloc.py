@@ -1,0 +1,90 @@
+"""GPU: the allocation-free decode entry point (split partials in the
+library's per-GPU scratch) against the entry point that takes a workspace,
+and against the oracle, on two calls in a row, the second with a smaller
+input; a forced split too large for the scratch is an error."""
+import pytest
+import torch
+
+from decode_attention_paged_06_amd import (paged_attention_decode, paged_attention_decode_noalloc,
+                                           paged_attention_plan, make_dims, make_opts, kv_layout_of)
+from decode_attention_paged_06_amd._lib import NOALLOC_SCRATCH_BYTES, PagedAttentionError
+from gpu_util import compare, device, make, oracle_ref, sample_seqs
+
+pytestmark = pytest.mark.gpu
+
+
+def both(inp, **kw):
+    """(noalloc output, workspace-entry-point output, plan) of one batch."""
+    a = torch.full_like(inp.query, float("nan"))
+    b = torch.full_like(inp.query, float("nan"))
+    args = (inp.query, inp.key_cache, inp.value_cache, inp.block_tables, inp.context_lens,
+            inp.scale, inp.block_size, inp.alibi_slopes)
+    paged_attention_decode_noalloc(a, *args, k_scale=inp.k_scale, v_scale=inp.v_scale, **kw)
+    paged_attention_decode(b, *args, k_scale=inp.k_scale, v_scale=inp.v_scale, **kw)
+    torch.cuda.synchronize()
+    dims = make_dims(inp.query, inp.key_cache, inp.block_tables, inp.k_scale, inp.v_scale,
+                     kv_layout_of(inp.key_cache, inp.value_cache))
+    plan = paged_attention_plan(dims, NOALLOC_SCRATCH_BYTES,
+                                make_opts(kw.get("partition_size", 0), kw.get("engine", "auto")))
+    return a, b, plan
+
+
+CASES = [
+    # (label, first batch, second (smaller) batch, call options)
+    ("gqa split", dict(num_seqs=4, num_heads=64, num_kv_heads=8, head_size=128, block_size=16,
+                       dtype="bf16", context_lens=4096),
+     dict(num_seqs=1, num_heads=64, num_kv_heads=8, head_size=128, block_size=16, dtype="bf16",
+          context_lens=1500), {}),
+    ("mqa ragged alibi, longest first",
+     dict(num_seqs=96, num_heads=48, num_kv_heads=1, head_size=128, block_size=16, dtype="f16",
+          context_lens=(64, 8192), alibi=True),
+     dict(num_seqs=20, num_heads=48, num_kv_heads=1, head_size=128, block_size=16, dtype="f16",
+          context_lens=(64, 3000), alibi=True), {}),
+    ("fp8 cache, forced partitions",
+     dict(num_seqs=8, num_heads=16, num_kv_heads=2, head_size=128, block_size=16, dtype="bf16",
+          context_lens=(1, 3000), kv_dtype="fp8", alibi=True),
+     dict(num_seqs=3, num_heads=16, num_kv_heads=2, head_size=128, block_size=16, dtype="bf16",
+          context_lens=[5, 300, 17], kv_dtype="fp8", alibi=True), dict(partition_size=128)),
+    ("valu engine, split", dict(num_seqs=2, num_heads=40, num_kv_heads=40, head_size=128,
+                                block_size=16, dtype="f16", context_lens=2048),
+     dict(num_seqs=1, num_heads=40, num_kv_heads=40, head_size=128, block_size=16, dtype="f16",
+          context_lens=700), dict(engine="valu", partition_size=256)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_noalloc_matches_workspace_entry_point(case):
+    label, first, second, kw = case
+    dev = device()
+    for k, shape in enumerate((first, second)):
+        inp = make(device_=dev, seed=900 + 10 * k + len(label), poison=True, kv_layout="joint",
+                   **shape)
+        a, b, plan = both(inp, **kw)
+        assert plan.num_partitions > 1 and plan.workspace_bytes <= NOALLOC_SCRATCH_BYTES, \
+            f"{label}: expected a split plan that uses the scratch"
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), \
+            f"{label} call {k}: the allocation-free entry point differs from the workspace one"
+        seqs = sample_seqs(inp.query.shape[0], 16, seed=k)
+        compare(a, oracle_ref(inp, seqs), inp.dtype, seqs,
+                what=f"{label} call {k} ({plan.num_partitions} partitions)")
+
+
+def test_noalloc_single_pass_and_oversized_split():
+    dev = device()
+    inp = make(device_=dev, num_seqs=64, num_heads=64, num_kv_heads=8, head_size=128, block_size=16,
+               dtype="bf16", seed=950, context_lens=1024, kv_layout="joint")
+    a, b, plan = both(inp)
+    assert plan.num_partitions == 1 and torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # 16-token partitions of a 65536-token bound for 4 x 64 heads: 512 MiB of partials
+    big = make(device_=dev, num_seqs=4, num_heads=64, num_kv_heads=1, head_size=128,
+               block_size=16, dtype="bf16", seed=951, context_lens=[100, 65536, 7, 3000])
+    out = torch.empty_like(big.query)
+    with pytest.raises(PagedAttentionError, match="scratch"):
+        paged_attention_decode_noalloc(out, big.query, big.key_cache, big.value_cache,
+                                       big.block_tables, big.context_lens, big.scale, 16,
+                                       partition_size=16)
+    # the auto plan of the same batch fits the scratch
+    paged_attention_decode_noalloc(out, big.query, big.key_cache, big.value_cache,
+                                   big.block_tables, big.context_lens, big.scale, 16)
+    torch.cuda.synchronize()
+    compare(out, oracle_ref(big), "bf16", what="auto plan of a 65536-token context, no allocation")
