@@ -68,6 +68,10 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="also time the calls replayed from a HIP graph (GPU time without the "
                          "host launch path; matters for small, launch-bound batches)")
+    ap.add_argument("--grid", action="store_true",
+                    help="also time every workload and batch of the configuration list (on by "
+                         "default for the headline invocation)")
+    ap.add_argument("--no-grid", action="store_true", help="skip the configuration grid")
     ap.add_argument("--context", type=int, default=4096, help="context per sequence for --op prefill")
     ap.add_argument("--new-tokens", type=int, default=512, help="new tokens per sequence for --op prefill")
     ap.add_argument("--op", default="decode", choices=["decode", "gather", "cache_write", "prefill"],
@@ -404,6 +408,167 @@ def cpu_baseline(args, budget_s):
             "seconds_per_sequence": round(dt / len(done), 4)}
 
 
+MAX_SETS = 1024   # cap on rotated input sets (tiny workloads: >= 1 GiB, 4x the last-level cache)
+# The pages' A100 kernel-latency tables (bf16, 64q/8kv): paged V1, paged V2, FlashAttention, in us.
+PAGES_TABLES_US = {
+    ("gqa_ctx1024", 1): (37.541, 29.602, 27.675), ("gqa_ctx1024", 4): (68.585, 71.447, 27.433),
+    ("gqa_ctx1024", 16): (162.237, 168.997, 67.681), ("gqa_ctx1024", 64): (687.938, 733.687, 214.041),
+    ("gqa_ctx1024", 256): (2215.532, 2378.606, 680.123),
+    ("gqa_ctx4096", 1): (137.858, 70.783, 28.557), ("gqa_ctx4096", 4): (223.438, 164.293, 62.104),
+    ("gqa_ctx4096", 16): (716.780, 724.601, 238.730), ("gqa_ctx4096", 64): (2324.863, 2792.657, 772.266),
+    ("gqa_ctx4096", 256): (8771.168, 9723.521, 2583.970),
+}
+
+
+def measure_decode(args, *, steps, warmup, engine="auto", partition_size=0, schedule="auto",
+                   hot=False, graph=False, per_call=True):
+    """Time paged_attention_decode on one synthetic workload (inputs resident in HBM).
+
+    Input sets with the same lengths and shapes are rotated so their combined
+    footprint is at least ROTATE_BYTES (at most MAX_SETS sets; one with
+    hot=True).  Eager time: HIP events around `steps` back-to-back calls (and
+    around each call when per_call).  graph=True also replays the calls from a
+    HIP graph: device time without the host launch path.
+    """
+    import torch
+
+    from decode_attention_paged_06_amd import (kv_layout_of, make_dims, make_opts,
+                                               paged_attention_decode, paged_attention_plan)
+    from workloads import algorithmic_bytes, algorithmic_flops, decode_inputs
+
+    dev = torch.device("cuda:0")
+    first = decode_inputs(device=dev, **args)
+    lens = first.context_lens.cpu().tolist()
+    nbytes = algorithmic_bytes(context_lens=lens, num_heads=args["num_heads"],
+                               num_kv_heads=args["num_kv_heads"], head_size=args["head_size"],
+                               block_size=args["block_size"], alibi=bool(args.get("alibi")),
+                               kv_elem_bytes=first.key_cache.element_size())
+    flops = algorithmic_flops(context_lens=lens, num_heads=args["num_heads"],
+                              head_size=args["head_size"])
+    footprint = sum(t.numel() * t.element_size() for t in
+                    (first.query, first.key_cache, first.value_cache, first.block_tables))
+    nsets = 1 if hot else min(MAX_SETS, max(1, -(-ROTATE_BYTES // footprint)))
+    sets = [first]
+    for i in range(1, nsets):
+        # same lengths and shapes, fresh values and block assignment
+        sets.append(decode_inputs(device=dev, **dict(args, seed=args["seed"] + 100000 * i,
+                                                      context_lens=lens)))
+    outs = [torch.empty_like(x.query) for x in sets]
+
+    dims = make_dims(first.query, first.key_cache, first.block_tables, first.k_scale,
+                     first.v_scale, kv_layout_of(first.key_cache, first.value_cache))
+    opts = make_opts(partition_size, engine, schedule=schedule)
+    plan = paged_attention_plan(dims, 1 << 40, opts)
+    workspace = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+                 if plan.workspace_bytes else None)
+
+    def step(i):
+        x = sets[i % nsets]
+        paged_attention_decode(outs[i % nsets], x.query, x.key_cache, x.value_cache,
+                               x.block_tables, x.context_lens, x.scale, x.block_size,
+                               x.alibi_slopes, workspace=workspace,
+                               partition_size=partition_size, engine=engine,
+                               k_scale=x.k_scale, v_scale=x.v_scale, schedule=schedule)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps if per_call else 0)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        if per_call:
+            ev[i][0].record()
+        step(i)
+        if per_call:
+            ev[i][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    res = {"nbytes": nbytes, "flops": flops, "plan": plan, "nsets": nsets, "wall": wall,
+           "ms_per_step": t_start.elapsed_time(t_end) / steps,
+           "per_call_ms": [x.elapsed_time(y) for x, y in ev]}
+
+    if graph:
+        # Capture one rotation of calls (at least 20) into a graph and replay it:
+        # the GPU then runs the kernels back to back, so the time is the
+        # device time of the calls without the host launch path.
+        ncap = max(20, nsets)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(ncap):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(ncap):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // ncap)
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        res["graph_us"] = g0.elapsed_time(g1) * 1e3 / (reps * ncap)
+        del g
+    del sets, outs, workspace, first
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def plan_fields(plan, engine="auto"):
+    return {"engine": {0: "auto", 1: "valu", 2: "mfma"}[plan.engine] if engine == "auto" else engine,
+            "num_partitions": plan.num_partitions, "partition_size": plan.partition_size,
+            "schedule": {2: "longest_first"}.get(plan.schedule, "grid")}
+
+
+def grid_rows(steps, warmup, kv_layout, headline=None):
+    """Every named workload at every batch the pages' tables (and the MQA and
+    MHA configurations) use: eager and graph-replay time per call, achieved
+    GB/s and the fraction of the 8 TB/s peak, and the plan.  `headline`
+    (workload, batch, measurement) is reused instead of measured again."""
+    from workloads import WORKLOADS, workload_args
+
+    rows = []
+    for name, w in WORKLOADS.items():
+        for batch in w["batches"]:
+            args = dict(workload_args(name, batch), kv_layout=kv_layout)
+            if headline is not None and (name, batch) == headline[:2]:
+                r = headline[2]
+            else:
+                r = measure_decode(args, steps=steps, warmup=warmup, graph=True, per_call=False)
+            us = r["ms_per_step"] * 1e3
+            row = {"workload": name, "batch": batch, "kv_cache": args["dtype"],
+                   "us_eager": round(us, 2),
+                   "GB/s_eager": round(r["nbytes"] / (us * 1e-6) / 1e9, 1),
+                   "frac_eager": round(r["nbytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+            if "graph_us" in r:
+                g = r["graph_us"]
+                row.update({"us_graph": round(g, 2),
+                            "GB/s_graph": round(r["nbytes"] / (g * 1e-6) / 1e9, 1),
+                            "frac_graph": round(r["nbytes"] / (g * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
+            row.update({"bytes": r["nbytes"], "input_sets": r["nsets"], **plan_fields(r["plan"])})
+            if (name, batch) in PAGES_TABLES_US:
+                v1, v2, fa = PAGES_TABLES_US[(name, batch)]
+                row["pages_a100_us"] = {"paged_v1": v1, "paged_v2": v2, "flash_attention": fa}
+            rows.append(row)
+            print(f"bench grid: {name} b={batch} eager {row['us_eager']} us, graph "
+                  f"{row.get('us_graph')} us", file=sys.stderr, flush=True)
+    return rows
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -425,9 +590,7 @@ def main():
 
     import torch
 
-    from decode_attention_paged_06_amd import (kv_layout_of, make_dims, make_opts,
-                                               paged_attention_decode, paged_attention_plan)
-    from workloads import HEADLINE, algorithmic_bytes, algorithmic_flops, decode_inputs, workload_args
+    from workloads import HEADLINE, workload_args
 
     name = a.workload or HEADLINE[0]
     batch = a.batch or HEADLINE[1]
@@ -441,97 +604,30 @@ def main():
         args.pop("max_blocks_per_seq", None)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    # the grid runs with the default headline invocation (and on request)
+    is_default = (a.workload is None and a.batch is None and not a.kv_dtype and not a.block_size
+                  and a.engine == "auto" and a.partition_size == 0 and a.schedule == "auto"
+                  and not a.hot)
+    want_grid = (is_default and not a.no_grid) or a.grid
 
-    first = decode_inputs(device=dev, **args)
-    lens = first.context_lens.cpu().tolist()
-    nbytes = algorithmic_bytes(context_lens=lens, num_heads=args["num_heads"],
-                               num_kv_heads=args["num_kv_heads"], head_size=args["head_size"],
-                               block_size=args["block_size"], alibi=bool(args.get("alibi")),
-                               kv_elem_bytes=first.key_cache.element_size())
-    flops = algorithmic_flops(context_lens=lens, num_heads=args["num_heads"],
-                              head_size=args["head_size"])
-    footprint = sum(t.numel() * t.element_size() for t in
-                    (first.query, first.key_cache, first.value_cache, first.block_tables))
-    nsets = 1 if a.hot else max(1, -(-ROTATE_BYTES // footprint))
-    sets = [first]
-    for i in range(1, nsets):
-        # same lengths and shapes, fresh values and block assignment
-        sets.append(decode_inputs(device=dev, **dict(args, seed=args["seed"] + 100000 * i,
-                                                      context_lens=lens)))
-    outs = [torch.empty_like(s.query) for s in sets]
-
-    dims = make_dims(first.query, first.key_cache, first.block_tables, first.k_scale,
-                     first.v_scale, kv_layout_of(first.key_cache, first.value_cache))
-    opts = make_opts(a.partition_size, a.engine, schedule=a.schedule)
-    plan = paged_attention_plan(dims, 1 << 40, opts)
-    workspace = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
-                 if plan.workspace_bytes else None)
-
-    def step(i):
-        s = sets[i % nsets]
-        paged_attention_decode(outs[i % nsets], s.query, s.key_cache, s.value_cache,
-                               s.block_tables, s.context_lens, s.scale, s.block_size,
-                               s.alibi_slopes, workspace=workspace,
-                               partition_size=a.partition_size, engine=a.engine,
-                               k_scale=s.k_scale, v_scale=s.v_scale, schedule=a.schedule)
-
-    for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(a.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(a.steps):
-        ev[i][0].record()
-        step(i)
-        ev[i][1].record()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
-    per_call_ms = [s.elapsed_time(e) for s, e in ev]
+    m = measure_decode(args, steps=a.steps, warmup=a.warmup, engine=a.engine,
+                       partition_size=a.partition_size, schedule=a.schedule, hot=a.hot,
+                       graph=a.graph or want_grid)
+    nbytes, flops, plan, nsets, wall = m["nbytes"], m["flops"], m["plan"], m["nsets"], m["wall"]
+    per_call_ms = m["per_call_ms"]
     avg_ms = sum(per_call_ms) / len(per_call_ms)
     srt = sorted(per_call_ms)
     per_call_us = {"median": round(srt[len(srt) // 2] * 1e3, 2), "min": round(srt[0] * 1e3, 2),
                    "max": round(srt[-1] * 1e3, 2)}
-    region_ms = t_start.elapsed_time(t_end)
-    ms_per_step = region_ms / a.steps
+    ms_per_step = m["ms_per_step"]
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    graph_us = m.get("graph_us")
 
-    graph_us = None
-    if a.graph:
-        # Capture one rotation of calls (at least 20) into a graph and replay it:
-        # the GPU then runs the kernels back to back, so the time is the
-        # device time of the calls without the host launch path.
-        ncap = max(20, nsets)
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(ncap):
-                step(i)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            for i in range(ncap):
-                step(i)
-        g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, a.steps // ncap)
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record()
-        for _ in range(reps):
-            g.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        graph_us = g0.elapsed_time(g1) * 1e3 / (reps * ncap)
+    grid = None
+    if want_grid:
+        grid = grid_rows(max(20, min(a.steps, 100)), min(a.warmup, 10), a.kv_layout,
+                         headline=(name, batch, m) if is_default else None)
 
     ceiling = None
     if not a.no_ceiling:
@@ -563,9 +659,7 @@ def main():
             "head_size": args["head_size"], "block_size": args["block_size"],
             "kv_cache": args.get("kv_dtype") or args["dtype"], "kv_layout": a.kv_layout,
             "context_lens": str(args["context_lens"]), "seed": args["seed"],
-            "engine": {0: "auto", 1: "valu", 2: "mfma"}[plan.engine] if a.engine == "auto" else a.engine,
-            "num_partitions": plan.num_partitions, "partition_size": plan.partition_size,
-            "schedule": {2: "longest_first"}.get(plan.schedule, "grid"),
+            **plan_fields(plan, a.engine),
             "input_sets_rotated": nsets,
             **({"hot_cache": True} if a.hot else {}),
         },
@@ -595,6 +689,13 @@ def main():
                                   "GB/s": round(nbytes / (graph_us * 1e-6) / 1e9, 2),
                                   "pct_of_hbm_peak": round(100 * nbytes / (graph_us * 1e-6) / 1e9
                                                            / HBM_PEAK_GBPS, 2)}
+    if grid is not None:
+        result["grid"] = {"note": "every workload and batch of the configuration list, "
+                                  f"{a.kv_layout} caches, auto plan; eager = HIP events around "
+                                  "back-to-back calls, graph = replay of captured calls (device "
+                                  "time without the host launch path); fractions of 8 TB/s; "
+                                  "pages_a100_us: the pages' A100 table entries (context)",
+                          "rows": grid}
     if ceiling is not None:
         result["device_ceiling"] = ceiling
     if context:
