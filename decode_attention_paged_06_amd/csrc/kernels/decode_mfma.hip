@@ -154,13 +154,26 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   constexpr int kRing = KT == 2 ? 3 : 4;  // ring slots (of KT tiles)
   // A staged tile: K as per-lane 16-byte pieces, V as the tile's own 16 rows
   // (contiguous in the cache), read back at the direct-load offsets.
+  //
+  // TRV (staged, 16-bit caches, D = 128): the P.V operand V^T is read from
+  // the ring with LDS transpose reads instead of being regrouped in
+  // registers.  A transpose read hands lane i of each 16-lane group element
+  // i % 4 of the 8-byte pieces that lanes i / 4 + 4 k (k = 0..3) point at, so
+  // with lane (group g, k, q) pointing at V row 4 g + k, dims 16 m + 4 q ..,
+  // lane (r, g) receives V[4 g + k][16 m + r], k = 0..3: the operand of
+  // output tile m (16 consecutive dims).  Rows are 256 bytes, so the 16-byte
+  // pieces of row t are stored XOR-swizzled by t (piece p at p ^ t), which
+  // spreads the 16 rows one read touches over all banks.
+  constexpr bool TRV = STAGE && !KV8 && D == 128;
   using KPiece = LdsPiece;
   constexpr int kVBytes = 16 * D * ES;
   constexpr int kStageBytes = NKL * KPiece::kBytes + kVBytes;
   constexpr int kTransfers = NKL * KPiece::kTransfers + kVBytes / 1024;  // per tile
   constexpr int kRingBytes = STAGE ? TG * kRing * KT * kStageBytes : 0;
   constexpr int ROWS = NT * RT * 16;  // query rows per workgroup (RT 16-row tiles per wave)
-  constexpr int kMergeBytes = TG > 1 ? NT * RT * (EPL * 64 * 16 + 2 * 64 * 4) : 0;
+  // token groups 1 .. TG - 1 each leave their softmax state in a slot
+  constexpr int kMergeSlotBytes = NT * RT * (EPL * 64 * 16 + 2 * 64 * 4);
+  constexpr int kMergeBytes = TG > 1 ? (TG - 1) * kMergeSlotBytes : 0;
   constexpr int kQueryBytes = ROWS * (D / 8) * 16;
   constexpr int kWorkBytes0 = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
   constexpr int kWorkBytes = kWorkBytes0 > kQueryBytes ? kWorkBytes0 : kQueryBytes;
@@ -306,6 +319,19 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
   const uint32_t k_lane = (uint32_t)(r * D * ES + j * 16);         // read-0 K chunk
   const uint32_t v_lane = (uint32_t)((4 * j) * D + r * EPL) * ES;  // load-0 V slice
+  // TRV: the V source offset of this lane in LDS transfer c (rows 4 c ..
+  // 4 c + 3; the transfer's own 1 KB step comes from its immediate offset),
+  // and the transpose-read offset of output tile m in a staged V tile
+  uint32_t v_swz[TRV ? 4 : 1], v_tr[TRV ? 8 : 1];
+  if constexpr (TRV) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      v_swz[c] = (uint32_t)(j * 256 + ((r ^ (4 * c + j)) & 15) * 16);
+    const int row = 4 * j + (r >> 2), q = r & 3;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      v_tr[m] = (uint32_t)(row * 256 + (((2 * m + (q >> 1)) ^ row) & 15) * 16 + (q & 1) * 8);
+  }
 
   // One 16-row tile's K and V in registers, as stored in the cache.
   struct Tile {
@@ -336,8 +362,9 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     }
   };
 
-  // T: KT consecutive tiles u0, u0 + 1, ...
-  auto process = [&](const Tile* T, int u0) {
+  // T: KT consecutive tiles u0, u0 + 1, ...; vlds (TRV): their staged V
+  // tiles, kStageBytes apart
+  auto process = [&](const Tile* T, int u0, const char* vlds) {
     // the compute format of the tiles (a no-op for 16-bit caches)
     uint4 kk[KT][NK];
     VT vv[KT][4];
@@ -345,8 +372,10 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
       for (int i = 0; i < NK; ++i) kk[kt][i] = KS::to16(T[kt].k[i]);
+      if constexpr (!TRV) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vv[kt][i] = KS::to16(T[kt].v[i]);
+        for (int i = 0; i < 4; ++i) vv[kt][i] = KS::to16(T[kt].v[i]);
+      }
     }
 
     // scores and weights of each row tile (the K tiles are shared)
@@ -389,7 +418,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
             x[kt][v] = (t < valid && tb + t <= pos[rt]) ? z : kNegBig;
           }
         }
-        local = fmaxf(local, xs[kt] * fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
+        local = score_max(local, xs[kt] * score_max(score_max(x[kt][0], x[kt][1]),
+                                                     score_max(x[kt][2], x[kt][3])));
       }
       // The reference max m moves only when some row's max over the step
       // exceeds it by more than kRescaleSlack (weights then stay below
@@ -397,7 +427,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       // the result is the same quotient acc / l whichever m it is taken against.
       const float mx = column_max4(local);
       if (wave_any(mx > m[rt] + kRescaleSlack)) {
-        const float mn = fmaxf(m[rt], mx);
+        const float mn = score_max(m[rt], mx);
         const float alpha = fast_exp2(m[rt] - mn);
         m[rt] = mn;
         lsum[rt] *= alpha;
@@ -424,14 +454,22 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     // weights above are laid out the same way)
 #pragma unroll
     for (int t = 0; t < EPL; ++t) {
-      const int w = t >> 1;
       uint2 vt[KT];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        const uint32_t a0 = VR::word(vv[kt][0], w), a1 = VR::word(vv[kt][1], w);
-        const uint32_t a2 = VR::word(vv[kt][2], w), a3 = VR::word(vv[kt][3], w);
-        vt[kt] = (t & 1) ? make_uint2(pack_hi_hi(a0, a1), pack_hi_hi(a2, a3))
-                         : make_uint2(pack_lo_lo(a0, a1), pack_lo_lo(a2, a3));
+        if constexpr (TRV) {
+          typedef short v4s_t __attribute__((ext_vector_type(4)));
+          typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+          const v4s_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4s_t*)(lds_void_t*)(vlds + kt * kStageBytes + v_tr[t]));
+          vt[kt] = __builtin_bit_cast(uint2, x);
+        } else {
+          const int w = t >> 1;
+          const uint32_t a0 = VR::word(vv[kt][0], w), a1 = VR::word(vv[kt][1], w);
+          const uint32_t a2 = VR::word(vv[kt][2], w), a3 = VR::word(vv[kt][3], w);
+          vt[kt] = (t & 1) ? make_uint2(pack_hi_hi(a0, a1), pack_hi_hi(a2, a3))
+                           : make_uint2(pack_lo_lo(a0, a1), pack_lo_lo(a2, a3));
+        }
       }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -464,7 +502,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
             const int uc = u + k * TG;
             load(buf[(k + kDepth - 1) % kDepth], uc + (kDepth - 1) * TG, blk_next);
             blk_next = block_of(uc + kDepth * TG);
-            process(&buf[k], uc);
+            process(&buf[k], uc, nullptr);
             more = uc + TG < ntiles;
           }
         }
@@ -497,13 +535,23 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     char* ring = work_lds + tg * (kRing * KT * kStageBytes);
     const bool issuer = tile == 0;
     // ring slots hold KT consecutive tiles: step unit us covers tiles
-    // us KT .. us KT + KT - 1 (those past the partition read nothing)
-    auto copy = [&](int us, int slot) {
+    // us KT .. us KT + KT - 1 (those past the partition read nothing).
+    // Their block ids come from the window; the issuer reads the next step's
+    // ids right after its copy (their LDS round trip then hides behind the
+    // step instead of queueing behind every wave's tile reads), except across
+    // a window refill.  An id outside the window is clamped into it and only
+    // ever used for a step that refills first (and reads its ids again).
+    auto window_ids = [&](int us, int* blk) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+        blk[kt] = tbl_lds[min(max(rel_block(us * KT + kt) - win0, 0), kTableWindow - 1)];
+    };
+    auto copy = [&](int us, int slot, const int* ids) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         const int u = us * KT + kt;
         const int ua = tile0 + u;
-        const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[rel_block(u) - win0]);
+        const int blk = __builtin_amdgcn_readfirstlane(ids[kt]);
         const size_t off = (size_t)blk * bstride + (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
         const uint32_t bytes = u < ntiles ? (uint32_t)min(tok1 - ua * TT, TT) * (D * ES) : 0u;
         const rsrc_t rk = make_rsrc(kbase + off, bytes);
@@ -511,41 +559,54 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
         char* dst = ring + (slot * KT + kt) * kStageBytes;
 #pragma unroll
         for (int i = 0; i < NKL; ++i) KPiece::copy(rk, k_lane + 64u * i, dst + i * KPiece::kBytes);
-        lds_copy_run<kVBytes>(rv, dst + NKL * KPiece::kBytes, lane);
+        if constexpr (TRV) lds_copy_rows_swizzled(rv, dst + NKL * KPiece::kBytes, v_swz);
+        else lds_copy_run<kVBytes>(rv, dst + NKL * KPiece::kBytes, lane);
       }
     };
     auto read = [&](Tile& T, int slot, int kt) {
       const char* src = ring + (slot * KT + kt) * kStageBytes;
 #pragma unroll
       for (int i = 0; i < NKL; ++i) KS::split(KPiece::read(src + i * KPiece::kBytes, lane), &T.k[i * KSTEP]);
+      if constexpr (!TRV) {  // (TRV: P.V reads V itself, transposed)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        T.v[i] = *reinterpret_cast<const VRaw*>(src + NKL * KPiece::kBytes + v_lane + (uint32_t)D * ES * i);
+        for (int i = 0; i < 4; ++i)
+          T.v[i] = *reinterpret_cast<const VRaw*>(src + NKL * KPiece::kBytes + v_lane + (uint32_t)D * ES * i);
+      }
     };
     const int nunits = (ntiles + KT - 1) / KT;
     const int nsteps = (nunits + TG - 1) / TG;
+    int ids[KT];
     if (issuer) {
 #pragma unroll
-      for (int k = 0; k + 1 < kRing; ++k) copy(tg + k * TG, k);
+      for (int k = 0; k + 1 < kRing; ++k) {
+        window_ids(tg + k * TG, ids);
+        copy(tg + k * TG, k, ids);
+      }
+      window_ids(tg + (kRing - 1) * TG, ids);  // step 0's
     }
     for (int j = 0; j < nsteps; ++j) {
       if (issuer) wait_vmcnt<kTransfers * KT * (kRing - 2)>();  // unit j has landed
       // the units copied in this step are (j + kRing - 1) TG + 0 .. TG - 1
       const int first = (j + kRing - 1) * TG;
-      if (rel_block((first + TG) * KT - 1) >= win0 + kTableWindow) {  // same for every wave
+      const bool refill = rel_block((first + TG) * KT - 1) >= win0 + kTableWindow;  // same for every wave
+      if (refill) {
         lds_barrier();  // every issuer is done with the old window
         win0 = rel_block(first * KT);
         fill_window(win0);
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       }
       lds_barrier();  // unit j is visible to every wave; slot (j - 1) % kRing is free
-      if (issuer) copy(tg + first, (j + kRing - 1) % kRing);
+      if (issuer) {
+        if (refill) window_ids(tg + first, ids);
+        copy(tg + first, (j + kRing - 1) % kRing, ids);
+        window_ids(tg + first + TG, ids);  // the next step's
+      }
       const int uc = tg + j * TG;
       if (uc < nunits) {
         Tile T[KT];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) read(T[kt], j % kRing, kt);
-        process(T, uc * KT);
+        process(T, uc * KT, ring + (j % kRing) * KT * kStageBytes + NKL * KPiece::kBytes);
       }
     }
     if (issuer) wait_vmcnt<0>();  // the copies past the end have landed before the LDS is reused
@@ -556,29 +617,38 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   for (int rt = 0; rt < RT; ++rt) lsum[rt] = column_sum4(lsum[rt]);
 
   // ---- merge the token groups into group 0 (fixed order: deterministic) ----
+  // Groups 1 .. TG - 1 write their states to their own slots at once; after
+  // a barrier group 0 folds them in, in group order (two barriers in all
+  // rather than two per group).
   if constexpr (TG > 1) {
-    auto mrg_acc = reinterpret_cast<f32x4_t(*)[EPL][64]>(work_lds);
-    auto mrg_m = reinterpret_cast<float(*)[64]>(work_lds + NT * RT * EPL * 64 * 16);
-    auto mrg_l = reinterpret_cast<float(*)[64]>(work_lds + NT * RT * EPL * 64 * 16 + NT * RT * 64 * 4);
-    for (int k = 1; k < TG; ++k) {
-      __syncthreads();
-      if (tg == k) {
+    __syncthreads();  // every wave is past its reads of the query / the ring, which the slots reuse
+    auto slot_base = [&](int k) { return work_lds + (k - 1) * kMergeSlotBytes; };
+    if (tg != 0) {
+      char* base = slot_base(tg);
+      auto mrg_acc = reinterpret_cast<f32x4_t(*)[EPL][64]>(base);
+      auto mrg_m = reinterpret_cast<float(*)[64]>(base + NT * RT * EPL * 64 * 16);
+      auto mrg_l = reinterpret_cast<float(*)[64]>(base + NT * RT * EPL * 64 * 16 + NT * RT * 64 * 4);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const int slot = tile * RT + rt;
-          mrg_m[slot][lane] = m[rt];
-          mrg_l[slot][lane] = lsum[rt];
+      for (int rt = 0; rt < RT; ++rt) {
+        const int slot = tile * RT + rt;
+        mrg_m[slot][lane] = m[rt];
+        mrg_l[slot][lane] = lsum[rt];
 #pragma unroll
-          for (int t = 0; t < EPL; ++t) mrg_acc[slot][t][lane] = acc[rt][t];
-        }
+        for (int t = 0; t < EPL; ++t) mrg_acc[slot][t][lane] = acc[rt][t];
       }
-      __syncthreads();
-      if (tg == 0) {
+    }
+    __syncthreads();
+    if (tg == 0) {
+      for (int k = 1; k < TG; ++k) {
+        const char* base = slot_base(k);
+        auto mrg_acc = reinterpret_cast<const f32x4_t(*)[EPL][64]>(base);
+        auto mrg_m = reinterpret_cast<const float(*)[64]>(base + NT * RT * EPL * 64 * 16);
+        auto mrg_l = reinterpret_cast<const float(*)[64]>(base + NT * RT * EPL * 64 * 16 + NT * RT * 64 * 4);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int slot = tile * RT + rt;
           const float mo = mrg_m[slot][lane];
-          const float mn = fmaxf(m[rt], mo);
+          const float mn = score_max(m[rt], mo);
           const float f = fast_exp2(m[rt] - mn);
           const float fo = fast_exp2(mo - mn);
           lsum[rt] = lsum[rt] * f + mrg_l[slot][lane] * fo;
@@ -601,27 +671,42 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     const size_t orow_idx = (size_t)(q_first + ti[rt]) * a.num_heads + h0 + g[rt];
     if (single || (part == 0 && pos[rt] < a.partition_blocks * BS)) {
       uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + orow_idx * D;
+      if constexpr (TRV) {  // output tile t: dims 16 t + 4 j .. + 3 of head r
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        uint32_t wv[EPL / 2];
+        for (int t = 0; t < EPL; ++t)
+          *reinterpret_cast<uint2*>(orow + 16 * t + 4 * j) =
+              make_uint2(Fmt::pack(acc[rt][t][0] * inv, acc[rt][t][1] * inv),
+                         Fmt::pack(acc[rt][t][2] * inv, acc[rt][t][3] * inv));
+      } else {  // output tiles: dims EPL (4 j + v) + t of head r
 #pragma unroll
-        for (int t = 0; t < EPL; t += 2)
-          wv[t / 2] = Fmt::pack(acc[rt][t][v] * inv, acc[rt][t + 1][v] * inv);
-        VT o;
-        if constexpr (EPL == 8) o = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-        else o = make_uint2(wv[0], wv[1]);
-        *reinterpret_cast<VT*>(orow + EPL * (4 * j + v)) = o;
+        for (int v = 0; v < 4; ++v) {
+          uint32_t wv[EPL / 2];
+#pragma unroll
+          for (int t = 0; t < EPL; t += 2)
+            wv[t / 2] = Fmt::pack(acc[rt][t][v] * inv, acc[rt][t + 1][v] * inv);
+          VT o;
+          if constexpr (EPL == 8) o = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+          else o = make_uint2(wv[0], wv[1]);
+          *reinterpret_cast<VT*>(orow + EPL * (4 * j + v)) = o;
+        }
       }
     } else {
       const size_t slot = orow_idx * a.num_partitions + part;
       float* orow = a.ws_o + slot * D;
+      if constexpr (TRV) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
+        for (int t = 0; t < EPL; ++t)
+          *reinterpret_cast<float4*>(orow + 16 * t + 4 * j) =
+              make_float4(acc[rt][t][0] * inv, acc[rt][t][1] * inv, acc[rt][t][2] * inv, acc[rt][t][3] * inv);
+      } else {
 #pragma unroll
-        for (int t = 0; t < EPL; t += 4)
-          *reinterpret_cast<float4*>(orow + EPL * (4 * j + v) + t) =
-              make_float4(acc[rt][t][v] * inv, acc[rt][t + 1][v] * inv, acc[rt][t + 2][v] * inv,
-                          acc[rt][t + 3][v] * inv);
+        for (int v = 0; v < 4; ++v) {
+#pragma unroll
+          for (int t = 0; t < EPL; t += 4)
+            *reinterpret_cast<float4*>(orow + EPL * (4 * j + v) + t) =
+                make_float4(acc[rt][t][v] * inv, acc[rt][t + 1][v] * inv, acc[rt][t + 2][v] * inv,
+                            acc[rt][t + 3][v] * inv);
+        }
       }
       if (j == 0) reinterpret_cast<float2*>(a.ws_ml)[slot] = make_float2(m[rt], lsum[rt]);
     }

@@ -171,8 +171,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
     for (int g = 0; g < GT; ++g) {
       float mx = x[g][0];
 #pragma unroll
-      for (int i = 1; i < NLOAD; ++i) mx = fmaxf(mx, x[g][i]);
-      const float mn = fmaxf(m[g], mx);
+      for (int i = 1; i < NLOAD; ++i) mx = score_max(mx, x[g][i]);
+      const float mn = score_max(m[g], mx);
       const float alpha = fast_exp2(m[g] - mn);
       m[g] = mn;
       float ps = 0.f;
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
     for (int off = TPT; off < 64; off <<= 1) {
       const float mo = shfl_xor(m[g], off);
       const float lo = shfl_xor(l[g], off);
-      const float mn = fmaxf(m[g], mo);
+      const float mn = score_max(m[g], mo);
       const float f = fast_exp2(m[g] - mn);
       const float fo = fast_exp2(mo - mn);
       l[g] = l[g] * f + lo * fo;
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(const DecodeAr
       for (int g = 0; g < GT; ++g) {
         const float mo = mrg_ml[g][0];
         const float lo = mrg_ml[g][1];
-        const float mn = fmaxf(m[g], mo);
+        const float mn = score_max(m[g], mo);
         const float f = fast_exp2(m[g] - mn);
         const float fo = fast_exp2(mo - mn);
         l[g] = l[g] * f + lo * fo;

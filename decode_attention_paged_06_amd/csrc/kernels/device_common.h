@@ -24,6 +24,15 @@ constexpr float kNegBig = -1.0e30f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum of two logits or running maxima, all of which lie below kPosBig
+// (masked scores are kNegBig; real logits are orders of magnitude smaller):
+// the median of the two and that ceiling, one v_med3_f32 with none of the
+// quieting steps that the IEEE maximum of arbitrary inputs (fmaxf) costs.
+constexpr float kPosBig = 1.0e30f;
+__device__ __forceinline__ float score_max(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, kPosBig);
+}
+
 // ---- 16-bit storage formats -------------------------------------------------
 
 struct F16 {
@@ -100,16 +109,17 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
 }
 
 // Reductions over the four lanes l % 16 + 16 k (k = 0..3) with the gfx950
-// lane-swap instructions: permlane32_swap pairs lane l with l ^ 32 and
+// lane-swap instructions (the maxima are of logits / running maxima, see
+// score_max): permlane32_swap pairs lane l with l ^ 32 and
 // permlane16_swap pairs it with l ^ 16.  Plain VALU moves, no LDS round trip;
 // every lane of a group ends with the same value (max and + are commutative).
 __device__ __forceinline__ float xor32_pair_max(float x) {
   const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  return score_max(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ __forceinline__ float xor16_pair_max(float x) {
   const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  return score_max(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ __forceinline__ float column_max4(float x) { return xor16_pair_max(xor32_pair_max(x)); }
 __device__ __forceinline__ float column_sum4(float x) {
@@ -239,6 +249,24 @@ __device__ __forceinline__ void lds_copy_run(rsrc_t r, char* dst, int lane) {
   } else {
     lds_load16(r, off, dst);
   }
+}
+
+// A 4 KB run of 16 rows of 256 bytes to dst, with each lane's source offset
+// in transfer c (rows 4 c .. 4 c + 3) given by voff[c]: transfer c's lane l
+// still lands at dst + 1024 c + 16 l, so the caller's offsets choose which
+// 16-byte piece of its row each LDS position holds (a swizzle).  One M0
+// set-up; the immediate offsets step memory and LDS by 1 KB per transfer.
+__device__ __forceinline__ void lds_copy_rows_swizzled(rsrc_t r, char* dst, const uint32_t* voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %5\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %6, 0 offen offset:0 nt lds\n\t"
+      "buffer_load_dwordx4 %2, %6, 0 offen offset:1024 nt lds\n\t"
+      "buffer_load_dwordx4 %3, %6, 0 offen offset:2048 nt lds\n\t"
+      "buffer_load_dwordx4 %4, %6, 0 offen offset:3072 nt lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(lds_address(dst)), "s"(r)
+      : "memory");
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.

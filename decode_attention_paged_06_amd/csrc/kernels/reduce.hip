@@ -25,12 +25,13 @@
 
 namespace pa {
 
-// Maximum / sum over the 64 lanes of a wave; every lane receives the result.
+// Maximum (of running maxima: finite) / sum over the 64 lanes of a wave;
+// every lane receives the result.
 __device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp<kDppQuadXor1>(x));
-  x = fmaxf(x, dpp<kDppQuadXor2>(x));
-  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
-  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  x = score_max(x, dpp<kDppQuadXor1>(x));
+  x = score_max(x, dpp<kDppQuadXor2>(x));
+  x = score_max(x, dpp<kDppRowHalfMirror>(x));
+  x = score_max(x, dpp<kDppRowMirror>(x));
   return column_max4(x);
 }
 __device__ __forceinline__ float wave_sum(float x) { return column_sum4(group_sum<16>(x)); }
@@ -54,7 +55,7 @@ __device__ __forceinline__ void weighted_sum(const float2* ml, const Part* o, in
   const float m0 = lane < nact ? s0.x : kNegBig;
   const float l0 = lane < nact ? s0.y : 0.f;
   float M = m0;
-  for (int c = 64; c < nact; c += 64) M = fmaxf(M, c + lane < nact ? ml[c + lane].x : kNegBig);
+  for (int c = 64; c < nact; c += 64) M = score_max(M, c + lane < nact ? ml[c + lane].x : kNegBig);
   M = wave_max(M);
 
   for (int c = 0; c < nact; c += 64) {
