@@ -24,6 +24,7 @@ SOURCES = [
     "host/api.cpp",
     "kernels/decode_valu.hip",
     "kernels/decode_mfma.hip",
+    "kernels/prefill_mfma32.hip",
     "kernels/reduce.hip",
     "kernels/gather.hip",
     "kernels/schedule.hip",

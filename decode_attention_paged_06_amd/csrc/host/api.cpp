@@ -365,9 +365,11 @@ int run_attention(void* out, const void* query, const void* key_cache, const voi
     if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "schedule launch: %s", hipGetErrorString(e));
     a.unit_order = order;
   }
-  hipError_t e = plan.engine == PA_ENGINE_MFMA
-                     ? pa::launch_decode_mfma(a, dims->dtype, dims->head_size, kv_fp8, s)
-                     : pa::launch_decode_valu(a, dims->dtype, dims->head_size, kv_fp8, s);
+  hipError_t e =
+      plan.engine != PA_ENGINE_MFMA ? pa::launch_decode_valu(a, dims->dtype, dims->head_size, kv_fp8, s)
+      : c.multi && pa::prefill_mfma32_supported(dims->head_size, kv_fp8, dims->block_size)
+          ? pa::launch_prefill_mfma32(a, dims->dtype, s)
+          : pa::launch_decode_mfma(a, dims->dtype, dims->head_size, kv_fp8, s);
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "attention launch: %s", hipGetErrorString(e));
   if (plan.num_partitions > 1) {
     e = pa::launch_partition_reduce(a, dims->dtype, dims->head_size, s);

@@ -78,6 +78,12 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, boo
                               hipStream_t s);
 hipError_t launch_partition_reduce(const DecodeArgs& a, int dtype, int head_size, hipStream_t s);
 
+// Multi-query calls on 32 x 32 matrix tiles (same grid, row chunks of
+// kPrefillRows, partials and reduce as the general kernel): 16-bit caches,
+// head size 128, blocks of at least 16 tokens.
+bool prefill_mfma32_supported(int head_size, bool kv_fp8, int block_size);
+hipError_t launch_prefill_mfma32(const DecodeArgs& a, int dtype, hipStream_t s);
+
 // Writes the num_seqs * num_partitions decode units (sequence, partition),
 // encoded partition * num_seqs + sequence, to `order` sorted by decreasing
 // token count (in buckets of partition_size / 62 tokens; order within a

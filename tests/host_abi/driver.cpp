@@ -160,10 +160,22 @@ static void prefill() {
                                 reinterpret_cast<const int32_t*>(FAKE),
                                 reinterpret_cast<const int32_t*>(FAKE + 128), T, maxq, 0.088f, 16,
                                 nullptr, nullptr, &d, w, ws, nullptr) == PA_OK);
-  CHECK(!g_launches.empty() && std::strcmp(g_launches[0].kind, "mfma") == 0);
+  // bf16, head size 128, 16-token blocks: the 32 x 32 tile kernel
+  CHECK(!g_launches.empty() && std::strcmp(g_launches[0].kind, "prefill32") == 0);
   const pa::DecodeArgs& a = g_launches[0].a;
   CHECK(a.query_start == reinterpret_cast<const int32_t*>(FAKE + 128));
   CHECK(a.max_new_tokens == maxq && a.row_chunks == (maxq * 8 + 127) / 128);
+  // 8-token blocks and head size 64 stay on the general kernel
+  for (int variant = 0; variant < 2; ++variant) {
+    g_launches.clear();
+    pa_dims e = variant == 0 ? dims(4, 64, 8, 128, 8, 65536, 512) : dims(4, 64, 8, 64);
+    const size_t wse = paged_attention_prefill_workspace_bytes(&e, T, maxq, nullptr);
+    CHECK(paged_attention_prefill(FAKE, FAKE, FAKE, FAKE + (1 << 28), reinterpret_cast<const int32_t*>(FAKE),
+                                  reinterpret_cast<const int32_t*>(FAKE),
+                                  reinterpret_cast<const int32_t*>(FAKE + 128), T, maxq, 0.088f,
+                                  e.block_size, nullptr, nullptr, &e, w, wse, nullptr) == PA_OK);
+    CHECK(!g_launches.empty() && std::strcmp(g_launches[0].kind, "mfma") == 0);
+  }
   pa_opts o = {0, PA_ENGINE_VALU, 0, PA_SCHEDULE_AUTO};
   CHECK(paged_attention_prefill(FAKE, FAKE, FAKE, FAKE + (1 << 28), reinterpret_cast<const int32_t*>(FAKE),
                                 reinterpret_cast<const int32_t*>(FAKE),

@@ -42,6 +42,13 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, boo
   record("mfma", &a, dtype, head_size, kv_fp8);
   return hipSuccess;
 }
+bool prefill_mfma32_supported(int head_size, bool kv_fp8, int block_size) {
+  return head_size == 128 && !kv_fp8 && block_size >= 16;
+}
+hipError_t launch_prefill_mfma32(const DecodeArgs& a, int dtype, hipStream_t) {
+  record("prefill32", &a, dtype, 128, false);
+  return hipSuccess;
+}
 hipError_t launch_partition_reduce(const DecodeArgs& a, int dtype, int head_size, hipStream_t) {
   record("reduce", &a, dtype, head_size, false);
   return hipSuccess;
