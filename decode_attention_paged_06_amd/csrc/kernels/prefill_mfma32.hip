@@ -28,9 +28,10 @@
 // operands, which is what lets S feed P.V without any data movement.
 //
 // LDS: a step's 32 key rows of K (8 KB) then of V (8 KB), 256 bytes per row,
-// each row's 16-byte pieces XOR-swizzled (K: by 2 (row % 8), V: by 4 (row %
-// 4)) so that the K reads (32 rows, two pieces each) and the V transpose
-// reads (8 rows, four pieces each) spread over all banks.  The swizzle is
+// each row's 16-byte pieces XOR-swizzled (K: by row % 16; V: by 5 (row % 4),
+// i.e. 0, 5, 10, 15) so that the lanes one LDS cycle serves -- 128 or 256
+// bytes' worth -- of a K read (rows n, pieces 2 s + jj) or of a V transpose
+// read (4 rows, 4 pieces) never share a bank.  The swizzle is
 // applied by the buffer-to-LDS copies themselves: each lane fetches the
 // piece that belongs at its fixed LDS position.
 //
@@ -40,6 +41,8 @@
 // matrix product and l sums the same rounded weights.  Built for 16-bit
 // caches, head size 128 and cache blocks of at least 16 tokens; other
 // multi-query calls run on the general kernel.
+#include <type_traits>
+
 #include "../launch.h"
 #include "device_common.h"
 
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
       v = reinterpret_cast<const uint4*>(a.q)[((size_t)(q_first + ti) * a.num_heads + h0 + row - ti * G) *
                                                   16 + piece];
     }
-    *reinterpret_cast<uint4*>(lds + rr * kRowBytes + ((piece ^ ((rr & 7) << 1)) << 4)) = v;
+    *reinterpret_cast<uint4*>(lds + rr * kRowBytes + ((piece ^ (rr & 15)) << 4)) = v;
   }
   __syncthreads();
   if (L <= 0) {  // no context: zero rows (a single pass writes them)
@@ -171,19 +174,19 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
 #pragma unroll
   for (int s = 0; s < 8; ++s)
     qb[s] = *reinterpret_cast<const uint4*>(lds + (32 * wave + n) * kRowBytes +
-                                            (((2 * s + jj) ^ ((n & 7) << 1)) << 4));
+                                            (((2 * s + jj) ^ (n & 15)) << 4));
 
   // LDS read offsets within a slot: K operand of k-step s; V transpose reads of
   // d-block b (key halves and sub-blocks are immediate offsets)
   uint32_t k_ofs[8], v_ofs[4];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) k_ofs[s] = n * kRowBytes + (((2 * s + jj) ^ ((n & 7) << 1)) << 4);
+  for (int s = 0; s < 8; ++s) k_ofs[s] = n * kRowBytes + (((2 * s + jj) ^ (n & 15)) << 4);
   {
     const int grp = lane >> 4, c = lane & 15, k = c >> 2, q = c & 3;
     const int vrow = 4 * (grp >> 1) + k;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
-      v_ofs[b] = kKBytes + vrow * kRowBytes + (((4 * b + 2 * (grp & 1) + (q >> 1)) ^ (k << 2)) << 4) +
+      v_ofs[b] = kKBytes + vrow * kRowBytes + (((4 * b + 2 * (grp & 1) + (q >> 1)) ^ (5 * k)) << 4) +
                  (q & 1) * 8;
   }
   // source offsets of the swizzled copies (transfer c = rows 4 c .. 4 c + 3)
@@ -192,8 +195,8 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
     const int rr = lane >> 4, piece = lane & 15;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      k_src[c] = rr * kRowBytes + ((piece ^ (((4 * c + rr) & 7) << 1)) << 4);
-      v_src[c] = rr * kRowBytes + ((piece ^ (rr << 2)) << 4);
+      k_src[c] = rr * kRowBytes + ((piece ^ (4 * c + rr)) << 4);
+      v_src[c] = rr * kRowBytes + ((piece ^ (5 * rr)) << 4);
     }
   }
 
@@ -249,28 +252,31 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       sc = Mfma32<Fmt>::mma(*reinterpret_cast<const uint4*>(slot + k_ofs[s]), qb[s], sc);
-    // logits in log2 units (or, for a step every row sees in full and no
-    // ALiBi, the raw scores with the positive scale applied in the exponent)
-    float x[16];
+    // logits in log2 units, in place (or, for a step every row sees in full
+    // and no ALiBi, the raw scores with the positive scale applied in the
+    // exponent: xs)
     float xs = 1.f;
     const bool full = kb + kKeys <= tok1 && kb + kKeys - 1 <= pos_lo;
     if (full && !has_alibi && a.scale_log2 > 0.f) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = sc[r];
       xs = a.scale_log2;
     } else {
       const float base = slope * (float)(kb + 4 * jj - pos);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + (r & 3);  // + 4 jj
-        const float z = fmaf(sc[r], a.scale_log2, fmaf((float)key, slope, base));
-        const int t = kb + key + 4 * jj;
-        x[r] = (full || (t < tok1 && t <= pos)) ? z : kNegBig;
+        sc[r] = fmaf(sc[r], a.scale_log2, fmaf((float)key, slope, base));
+      }
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = kb + 8 * (r >> 2) + (r & 3) + 4 * jj;
+          sc[r] = (t < tok1 && t <= pos) ? sc[r] : kNegBig;
+        }
       }
     }
-    float mx = x[0];
+    float mx = sc[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = score_max(mx, x[r]);
+    for (int r = 1; r < 16; ++r) mx = score_max(mx, sc[r]);
     mx = xor32_pair_max(mx * xs);
     if (wave_any(mx > m + kRescaleSlack)) {
       const float mn = score_max(m, mx);
@@ -284,7 +290,7 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
     uint32_t pw[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      pw[q] = Fmt::pack(fast_exp2(fmaf(x[2 * q], xs, nm)), fast_exp2(fmaf(x[2 * q + 1], xs, nm)));
+      pw[q] = Fmt::pack(fast_exp2(fmaf(sc[2 * q], xs, nm)), fast_exp2(fmaf(sc[2 * q + 1], xs, nm)));
       lsum = Fmt::dot2(pw[q], Fmt::kOnes, lsum);  // l sums the rounded weights P.V uses
     }
     // P.V over the two key halves
@@ -314,7 +320,11 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
     }
     window_ids(kSlots - 1, ids);
   }
-  for (int j = 0; j < nsteps; ++j) {
+  // One step; the ring slot is a compile-time constant (the loop below is
+  // unrolled by the ring size), so every LDS operand address is a lane offset
+  // plus an immediate.
+  auto step = [&](int j, auto slot_tag) {
+    constexpr int kSlot = decltype(slot_tag)::value;
     if (issuer) wait_vmcnt<kTransfersPerStep * (kSlots - 2)>();  // step j has landed
     const int jc = j + kSlots - 1;  // the step copied now
     const bool refill = rel_block(2 * jc + 1) >= win0 + kWindow;  // same for every wave
@@ -327,13 +337,19 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
     lds_barrier();  // step j is visible to every wave; slot (j - 1) % kSlots is free
     if (issuer) {
       if (refill) window_ids(jc, ids);
-      copy(jc, jc % kSlots, ids);
+      copy(jc, (kSlot + kSlots - 1) % kSlots, ids);
       window_ids(jc + 1, ids);
     }
     const int kb = tok0 + j * kKeys;
     // (wave-uniform: a wave whose rows are all padding, or sit before every key
     // of the step, has nothing to add)
-    if (wrow0 < nrows && kb <= pos_hi) process(lds + (j % kSlots) * kSlotBytes, kb);
+    if (wrow0 < nrows && kb <= pos_hi) process(lds + kSlot * kSlotBytes, kb);
+  };
+  static_assert(kSlots == 3, "the loop is unrolled by the ring size");
+  for (int j = 0; j < nsteps; j += kSlots) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nsteps) step(j + 1, std::integral_constant<int, 1>{});
+    if (j + 2 < nsteps) step(j + 2, std::integral_constant<int, 2>{});
   }
   if (issuer) wait_vmcnt<0>();  // copies past the end have landed before the workgroup ends
 
