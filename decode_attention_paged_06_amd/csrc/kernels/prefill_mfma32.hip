@@ -10,7 +10,7 @@
 // (sequence, kv head) -- row i G + g is new token i, query head g of the
 // group -- and walks the keys they see in steps of 32 (two 16-row cache
 // tiles), staged once per step through an LDS ring of three slots that all
-// four waves read.  Wave w owns rows 32 w .. 32 w + 31 and computes, per step,
+// four waves fill (a quarter each) and read.  Wave w owns rows 32 w .. 32 w + 31 and computes, per step,
 //   S^T[key, row]  = sum_d K[key, d] Q[row, d]     8 x v_mfma_f32_32x32x16 (D / 16)
 //   O^T[d, row]   += sum_key V[key, d] P[row, key]  8 x v_mfma_f32_32x32x16 (4 d-blocks x 2)
 // Register layouts (lane = 32 jj + n):
@@ -82,7 +82,7 @@ constexpr int kRingBytes = kSlots * kSlotBytes;
 constexpr int kQBytes = kRows * kRowBytes;     // 32 KB: the query rows, before the ring
 constexpr int kLdsBytes = kRingBytes > kQBytes ? kRingBytes : kQBytes;
 constexpr int kWindow = 512;                   // block-table entries kept in LDS
-constexpr int kTransfersPerStep = 16;          // 2 tiles x (4 K + 4 V) 1 KB copies
+constexpr int kTransfersPerWave = 4;           // 1 KB copies per wave per step (a quarter)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;
 
@@ -217,24 +217,22 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
   fill_window(0);
   __syncthreads();
 
-  const bool issuer = wave == 0;
-  // step j: tiles 2 j, 2 j + 1 (those past the partition read nothing)
-  auto window_ids = [&](int j, int* ids) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) ids[kt] = tbl[min(max(rel_block(2 * j + kt) - win0, 0), kWindow - 1)];
-  };
-  auto copy = [&](int j, int slot, const int* ids) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int u = 2 * j + kt;
-      const int ua = tile0 + u;
-      const int blk = __builtin_amdgcn_readfirstlane(ids[kt]);
-      const size_t off = (size_t)blk * bstride + (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * kRowBytes);
-      const uint32_t bytes = u < ntiles ? (uint32_t)min(tok1 - ua * 16, 16) * kRowBytes : 0u;
-      char* dst = lds + slot * kSlotBytes + kt * 16 * kRowBytes;
-      copy_tile(make_rsrc(kbase + off, bytes), dst, k_src);
-      copy_tile(make_rsrc(vbase + off, bytes), dst + kKBytes, v_src);
-    }
+  // Every wave copies a quarter of each step: wave w the K (w even) or V (w
+  // odd) rows of the step's tile w / 2 -- four 1 KB transfers -- so the copy
+  // work and its scalar address arithmetic are shared evenly.  Tiles past the
+  // partition read nothing (zeros).
+  const int my_kt = wave >> 1;
+  const bool my_v = (wave & 1) != 0;
+  const char* my_base = my_v ? vbase : kbase;
+  auto window_id = [&](int j) { return tbl[min(max(rel_block(2 * j + my_kt) - win0, 0), kWindow - 1)]; };
+  auto copy = [&](int j, int slot, int id) {
+    const int u = 2 * j + my_kt;
+    const int ua = tile0 + u;
+    const int blk = __builtin_amdgcn_readfirstlane(id);
+    const size_t off = (size_t)blk * bstride + (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * kRowBytes);
+    const uint32_t bytes = u < ntiles ? (uint32_t)min(tok1 - ua * 16, 16) * kRowBytes : 0u;
+    char* dst = lds + slot * kSlotBytes + (my_v ? kKBytes : 0) + my_kt * 16 * kRowBytes;
+    copy_tile(make_rsrc(my_base + off, bytes), dst, my_v ? v_src : k_src);
   };
 
   float m = kNegBig, lsum = 0.f;
@@ -311,35 +309,27 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
   };
 
   // ---- the staged loop: slot j % kSlots holds step j ------------------------
-  int ids[2];
-  if (issuer) {
+  int id = 0;
 #pragma unroll
-    for (int k = 0; k + 1 < kSlots; ++k) {
-      window_ids(k, ids);
-      copy(k, k, ids);
-    }
-    window_ids(kSlots - 1, ids);
-  }
+  for (int k = 0; k + 1 < kSlots; ++k) copy(k, k, window_id(k));
+  id = window_id(kSlots - 1);
   // One step; the ring slot is a compile-time constant (the loop below is
   // unrolled by the ring size), so every LDS operand address is a lane offset
   // plus an immediate.
   auto step = [&](int j, auto slot_tag) {
     constexpr int kSlot = decltype(slot_tag)::value;
-    if (issuer) wait_vmcnt<kTransfersPerStep * (kSlots - 2)>();  // step j has landed
+    wait_vmcnt<kTransfersPerWave * (kSlots - 2)>();  // this wave's part of step j has landed
     const int jc = j + kSlots - 1;  // the step copied now
     const bool refill = rel_block(2 * jc + 1) >= win0 + kWindow;  // same for every wave
     if (refill) {
-      lds_barrier();  // the issuer is done with the old window
+      lds_barrier();  // every wave is done with the old window
       win0 = rel_block(2 * jc);
       fill_window(win0);
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     }
     lds_barrier();  // step j is visible to every wave; slot (j - 1) % kSlots is free
-    if (issuer) {
-      if (refill) window_ids(jc, ids);
-      copy(jc, (kSlot + kSlots - 1) % kSlots, ids);
-      window_ids(jc + 1, ids);
-    }
+    copy(jc, (kSlot + kSlots - 1) % kSlots, refill ? window_id(jc) : id);
+    id = window_id(jc + 1);
     const int kb = tok0 + j * kKeys;
     // (wave-uniform: a wave whose rows are all padding, or sit before every key
     // of the step, has nothing to add)
@@ -351,7 +341,7 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
     if (j + 1 < nsteps) step(j + 1, std::integral_constant<int, 1>{});
     if (j + 2 < nsteps) step(j + 2, std::integral_constant<int, 2>{});
   }
-  if (issuer) wait_vmcnt<0>();  // copies past the end have landed before the workgroup ends
+  wait_vmcnt<0>();  // copies past the end have landed before the workgroup ends
 
   // ---- finalise ---------------------------------------------------------------
   // l: this lane's keys plus its partner lane's (n, 1 - jj)
