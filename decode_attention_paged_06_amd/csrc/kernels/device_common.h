@@ -256,17 +256,30 @@ __device__ __forceinline__ void lds_copy_run(rsrc_t r, char* dst, int lane) {
 // still lands at dst + 1024 c + 16 l, so the caller's offsets choose which
 // 16-byte piece of its row each LDS position holds (a swizzle).  One M0
 // set-up; the immediate offsets step memory and LDS by 1 KB per transfer.
+template <bool NT = true>
 __device__ __forceinline__ void lds_copy_rows_swizzled(rsrc_t r, char* dst, const uint32_t* voff) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %5\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %6, 0 offen offset:0 nt lds\n\t"
-      "buffer_load_dwordx4 %2, %6, 0 offen offset:1024 nt lds\n\t"
-      "buffer_load_dwordx4 %3, %6, 0 offen offset:2048 nt lds\n\t"
-      "buffer_load_dwordx4 %4, %6, 0 offen offset:3072 nt lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(lds_address(dst)), "s"(r)
-      : "memory");
+  if constexpr (NT) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %5\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %6, 0 offen offset:0 nt lds\n\t"
+        "buffer_load_dwordx4 %2, %6, 0 offen offset:1024 nt lds\n\t"
+        "buffer_load_dwordx4 %3, %6, 0 offen offset:2048 nt lds\n\t"
+        "buffer_load_dwordx4 %4, %6, 0 offen offset:3072 nt lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(lds_address(dst)), "s"(r)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %5\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %6, 0 offen offset:0 lds\n\t"
+        "buffer_load_dwordx4 %2, %6, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %3, %6, 0 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %4, %6, 0 offen offset:3072 lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(lds_address(dst)), "s"(r)
+        : "memory");
+  }
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.

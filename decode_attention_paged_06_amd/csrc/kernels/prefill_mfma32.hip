@@ -81,7 +81,7 @@ constexpr int kSlots = 3;                      // ring slots
 constexpr int kRingBytes = kSlots * kSlotBytes;
 constexpr int kQBytes = kRows * kRowBytes;     // 32 KB: the query rows, before the ring
 constexpr int kLdsBytes = kRingBytes > kQBytes ? kRingBytes : kQBytes;
-constexpr int kWindow = 512;                   // block-table entries kept in LDS
+constexpr int kWindow = 512;                   // tile source offsets kept in LDS
 constexpr int kTransfersPerWave = 4;           // 1 KB copies per wave per step (a quarter)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;
@@ -90,7 +90,7 @@ constexpr float kRescaleSlack = 8.f;
 // l of transfer c fetches the source bytes at voff[c] (+ 1 KB c) for LDS
 // position dst + 1 KB c + 16 l.
 __device__ __forceinline__ void copy_tile(rsrc_t r, char* dst, const uint32_t* voff) {
-  lds_copy_rows_swizzled(r, dst, voff);
+  lds_copy_rows_swizzled<false>(r, dst, voff);
 }
 
 }  // namespace
@@ -98,7 +98,7 @@ __device__ __forceinline__ void copy_tile(rsrc_t r, char* dst, const uint32_t* v
 template <typename Fmt>
 __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArgs a) {
   __shared__ __align__(16) char lds[kLdsBytes];
-  __shared__ int tbl[kWindow];
+  __shared__ uint64_t toff[kWindow];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -200,19 +200,28 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
     }
   }
 
-  const size_t bstride = (size_t)a.kv_block_stride;
   const size_t head_off = (size_t)kvh * (size_t)a.kv_head_stride;
   const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
 
-  // block-table window
-  const int b0 = tile0 >> tpb_shift;
-  const int nblk = ((tile0 + ntiles - 1) >> tpb_shift) - b0 + 1;
+  // Source offsets of the partition's 16-row tiles (block-table entry times
+  // the block stride, plus the tile's place in its block), kWindow tiles at a
+  // time: the lookup and the 64-bit product are done here once per tile, by
+  // all lanes, and a step's copy only adds its base.  Entries past the last
+  // tile repeat it (their copies read nothing).
+  const uint64_t bstride = (uint64_t)a.kv_block_stride;
+  const int tpb_mask = (1 << tpb_shift) - 1;
   auto fill_window = [&](int start) {
-    for (int i = threadIdx.x; i < kWindow; i += kW * 64) tbl[i] = start + i < nblk ? table[b0 + start + i] : 0;
+    for (int i = threadIdx.x; i < kWindow; i += kW * 64) {
+      const int ua = tile0 + min(start + i, ntiles - 1);
+      toff[i] = (uint64_t)(uint32_t)table[ua >> tpb_shift] * bstride + (uint32_t)((ua & tpb_mask) << 12);
+    }
   };
-  auto rel_block = [&](int u) { return ((tile0 + min(u, ntiles - 1)) >> tpb_shift) - b0; };
+  // the window starts at tile win0; the first step whose second tile lies
+  // past it refills it (never, once the window reaches the last tile)
   int win0 = 0;
+  auto refill_step = [&](int w0) { return ntiles - 1 - w0 < kWindow ? 0x7fffffff : (w0 + kWindow) / 2; };
+  int refill_at = refill_step(0);
   __syncthreads();  // every wave has its query rows: the LDS becomes the ring
   fill_window(0);
   __syncthreads();
@@ -224,15 +233,15 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
   const int my_kt = wave >> 1;
   const bool my_v = (wave & 1) != 0;
   const char* my_base = my_v ? vbase : kbase;
-  auto window_id = [&](int j) { return tbl[min(max(rel_block(2 * j + my_kt) - win0, 0), kWindow - 1)]; };
-  auto copy = [&](int j, int slot, int id) {
+  // (tiles at or after win0: the index is never negative)
+  auto window_off = [&](int j) { return toff[min(min(2 * j + my_kt, ntiles - 1) - win0, kWindow - 1)]; };
+  auto copy = [&](int j, int slot, uint64_t off) {
     const int u = 2 * j + my_kt;
-    const int ua = tile0 + u;
-    const int blk = __builtin_amdgcn_readfirstlane(id);
-    const size_t off = (size_t)blk * bstride + (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * kRowBytes);
-    const uint32_t bytes = u < ntiles ? (uint32_t)min(tok1 - ua * 16, 16) * kRowBytes : 0u;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)off);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(off >> 32));
+    const uint32_t bytes = u < ntiles ? (uint32_t)min(tok1 - (tile0 + u) * 16, 16) * kRowBytes : 0u;
     char* dst = lds + slot * kSlotBytes + (my_v ? kKBytes : 0) + my_kt * 16 * kRowBytes;
-    copy_tile(make_rsrc(my_base + off, bytes), dst, my_v ? v_src : k_src);
+    copy_tile(make_rsrc(my_base + (((uint64_t)hi << 32) | lo), bytes), dst, my_v ? v_src : k_src);
   };
 
   float m = kNegBig, lsum = 0.f;
@@ -242,14 +251,17 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
 
-  auto process = [&](const char* slot, int kb) {
-    // scores S^T of the step: 16 keys of row n per lane
+  // scores S^T of a step: 16 keys of row n per lane
+  auto scores = [&](const char* slot) {
     f32x16_t sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       sc = Mfma32<Fmt>::mma(*reinterpret_cast<const uint4*>(slot + k_ofs[s]), qb[s], sc);
+    return sc;
+  };
+  auto process = [&](const char* slot, int kb, f32x16_t sc) {
     // logits in log2 units, in place (or, for a step every row sees in full
     // and no ALiBi, the raw scores with the positive scale applied in the
     // exponent: xs)
@@ -309,10 +321,9 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
   };
 
   // ---- the staged loop: slot j % kSlots holds step j ------------------------
-  int id = 0;
 #pragma unroll
-  for (int k = 0; k + 1 < kSlots; ++k) copy(k, k, window_id(k));
-  id = window_id(kSlots - 1);
+  for (int k = 0; k + 1 < kSlots; ++k) copy(k, k, window_off(k));
+  uint64_t off_next = window_off(kSlots - 1);
   // One step; the ring slot is a compile-time constant (the loop below is
   // unrolled by the ring size), so every LDS operand address is a lane offset
   // plus an immediate.
@@ -320,20 +331,26 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
     constexpr int kSlot = decltype(slot_tag)::value;
     wait_vmcnt<kTransfersPerWave * (kSlots - 2)>();  // this wave's part of step j has landed
     const int jc = j + kSlots - 1;  // the step copied now
-    const bool refill = rel_block(2 * jc + 1) >= win0 + kWindow;  // same for every wave
+    const bool refill = jc >= refill_at;  // same for every wave
     if (refill) {
       lds_barrier();  // every wave is done with the old window
-      win0 = rel_block(2 * jc);
+      win0 = 2 * jc;
+      refill_at = refill_step(win0);
       fill_window(win0);
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     }
     lds_barrier();  // step j is visible to every wave; slot (j - 1) % kSlots is free
-    copy(jc, (kSlot + kSlots - 1) % kSlots, refill ? window_id(jc) : id);
-    id = window_id(jc + 1);
     const int kb = tok0 + j * kKeys;
     // (wave-uniform: a wave whose rows are all padding, or sit before every key
     // of the step, has nothing to add)
-    if (wrow0 < nrows && kb <= pos_hi) process(lds + kSlot * kSlotBytes, kb);
+    const bool work = wrow0 < nrows && kb <= pos_hi;
+    // the scores' matrix products are issued before the copy, whose scalar
+    // address arithmetic then overlaps them
+    f32x16_t sc;
+    if (work) sc = scores(lds + kSlot * kSlotBytes);
+    copy(jc, (kSlot + kSlots - 1) % kSlots, refill ? window_off(jc) : off_next);
+    off_next = window_off(jc + 1);
+    if (work) process(lds + kSlot * kSlotBytes, kb, sc);
   };
   static_assert(kSlots == 3, "the loop is unrolled by the ring size");
   for (int j = 0; j < nsteps; j += kSlots) {

@@ -120,3 +120,46 @@ def test_prefill_bench_shape_sampled(kv):
                               tables, lens, inp.scale, inp.block_size, None, dtype="bf16",
                               k_scale=inp.k_scale, v_scale=inp.v_scale)
     compare(out[rows], ref, "bf16", what=f"prefill bench shape ({kv or 'bf16'} cache), sampled rows")
+
+
+# Calls on 32 x 32 matrix tiles: head size 128, 16-bit caches, blocks of at
+# least 16 tokens (the dispatch rule of the library).  Row chunks of 128 rows
+# with a group that does not divide them, ragged tails, several cache block
+# sizes (a block holds 1, 2 or 16 of the kernel's 16-row tiles), ALiBi, and
+# forced single-pass and split plans.
+P32_CASES = [
+    # (name, heads, kv heads, dtype, block, lengths, new tokens, alibi)
+    ("p32-gqa-bs16-alibi", 16, 2, "bf16", 16, [300, 1000, 77], [129, 300, 77], True),
+    ("p32-bs32-f16", 32, 4, "f16", 32, [513, 64], [200, 64], False),
+    ("p32-bs256", 8, 1, "bf16", 256, [700, 2100], [150, 33], True),
+    ("p32-mqa48", 48, 1, "bf16", 16, [400, 45], [100, 45], True),
+]
+
+
+@pytest.mark.parametrize("case", P32_CASES, ids=[c[0] for c in P32_CASES])
+def test_prefill32_parity(case):
+    dev = device()
+    name, Hq, Hkv, dtype, BS, lens, news, alibi = case
+    inp, q, qs, max_q = prefill_inputs(new_tokens=news, seed=len(name) + sum(lens), device=dev,
+                                       num_seqs=len(lens), num_heads=Hq, num_kv_heads=Hkv,
+                                       head_size=128, block_size=BS, dtype=dtype,
+                                       context_lens=lens, alibi=alibi, poison=True)
+    ref = ref_prefill(inp, q, qs)
+    for ps in (-1, 0, max(BS, 256)):
+        compare(run_prefill(inp, q, qs, max_q, ps), ref, dtype, what=f"{name} partition={ps}")
+
+
+@pytest.mark.parametrize("BS", [16, 64])
+def test_prefill32_window_refill(BS):
+    """One pass over more than the 512 tiles (8192 tokens) whose source offsets
+    the kernel keeps in LDS at a time, so the window is refilled mid-loop."""
+    dev = device()
+    lens = [9000, 8450]
+    news = [33, 3]
+    inp, q, qs, max_q = prefill_inputs(new_tokens=news, seed=21 + BS, device=dev, num_seqs=2,
+                                       num_heads=8, num_kv_heads=1, head_size=128,
+                                       block_size=BS, dtype="bf16", context_lens=lens,
+                                       alibi=True, poison=True)
+    ref = ref_prefill(inp, q, qs)
+    for ps in (-1, 0):
+        compare(run_prefill(inp, q, qs, max_q, ps), ref, "bf16", what=f"refill BS={BS} partition={ps}")
