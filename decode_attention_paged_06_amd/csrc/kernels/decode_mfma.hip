@@ -162,13 +162,14 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   // with lane (group g, k, q) pointing at V row 4 g + k, dims 16 m + 4 q ..,
   // lane (r, g) receives V[4 g + k][16 m + r], k = 0..3: the operand of
   // output tile m (16 consecutive dims).  Rows are 256 bytes, so the 16-byte
-  // pieces of row t are stored XOR-swizzled by t (piece p at p ^ t), which
-  // spreads the 16 rows one read touches over all banks.
+  // pieces of row t are stored XOR-swizzled by 2 t (piece p at p ^ 2 t mod
+  // 16): a read's lanes want pieces 2 m and 2 m + 1 of 4 (per 128 bytes the
+  // LDS serves) or 8 (per 256) consecutive rows, and those land on distinct
+  // 8-byte bank slots, so no read waits on a bank conflict.
   constexpr bool TRV = STAGE && !KV8 && D == 128;
   using KPiece = LdsPiece;
   constexpr int kVBytes = 16 * D * ES;
   constexpr int kStageBytes = NKL * KPiece::kBytes + kVBytes;
-  constexpr int kTransfers = NKL * KPiece::kTransfers + kVBytes / 1024;  // per tile
   constexpr int kRingBytes = STAGE ? TG * kRing * KT * kStageBytes : 0;
   constexpr int ROWS = NT * RT * 16;  // query rows per workgroup (RT 16-row tiles per wave)
   // token groups 1 .. TG - 1 each leave their softmax state in a slot
@@ -180,8 +181,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   // the query rows before the tile loop (they move to registers first), the
   // ring during it, the token-group merge after it
   __shared__ __align__(16) char work_lds[kWorkBytes];
-  constexpr int kTableWindow = 512;  // block-table entries held in LDS by the staged loop
-  __shared__ int tbl_lds[STAGE ? kTableWindow : 1];
+  constexpr int kTableWindow = 512;  // tile source offsets held in LDS by the staged loop
+  __shared__ uint64_t toff_lds[STAGE ? kTableWindow : 1];
 
   constexpr int NTHREADS = NT * TG * 64;
   const int lane = threadIdx.x & 63;
@@ -326,11 +327,11 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   if constexpr (TRV) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      v_swz[c] = (uint32_t)(j * 256 + ((r ^ (4 * c + j)) & 15) * 16);
+      v_swz[c] = (uint32_t)(j * 256 + ((r ^ (2 * (4 * c + j))) & 15) * 16);
     const int row = 4 * j + (r >> 2), q = r & 3;
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-      v_tr[m] = (uint32_t)(row * 256 + (((2 * m + (q >> 1)) ^ row) & 15) * 16 + (q & 1) * 8);
+      v_tr[m] = (uint32_t)(row * 256 + (((2 * m + (q >> 1)) ^ (2 * row)) & 15) * 16 + (q & 1) * 8);
   }
 
   // One 16-row tile's K and V in registers, as stored in the cache.
@@ -512,51 +513,59 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   } else {
     // LDS ring: the first wave of each token group copies tile tg + j TG into
     // slot j % kRing, kRing - 1 tiles ahead; after its wait and a barrier
-    // every wave of the group reads the tile from the slot.  All waves of the
-    // workgroup run the same number of steps (every step has a barrier); a
-    // group's steps past its last tile copy nothing and process nothing.
+    // every wave of the group reads the tile from the slot (splitting the
+    // copy between two waves, K and V, measured no faster).  All waves of the workgroup run the same number of steps
+    // (every step has a barrier); a group's steps past its last tile copy
+    // nothing and process nothing.
     //
-    // Block ids come from a window of the partition's table entries kept in
-    // LDS (the copies write memory the compiler cannot tell apart from the
-    // table, so the table is not read with scalar loads inside the loop).
-    // The window is refilled by all waves, between barriers, when the tiles
-    // being copied move past it.
-    const int b0 = tile0 >> tpb_shift;                          // first block of the partition
-    const int nblk = ((tile0 + ntiles - 1) >> tpb_shift) - b0 + 1;  // blocks it uses
+    // Source offsets of the partition's tiles (block-table entry times the
+    // block stride, plus the tile's place in its block) come from a window of
+    // kTableWindow tiles kept in LDS: the table lookup and the 64-bit product
+    // are done once per tile, by all lanes, when the window is filled, and a
+    // step's copy only adds its base.  Entries past the last tile repeat it
+    // (their copies read nothing).  The copies write memory the compiler
+    // cannot tell apart from the table, so the table is not read with scalar
+    // loads inside the loop.  The window is refilled by all waves, between
+    // barriers, when the tiles being copied move past it.
+    const uint64_t bstride64 = (uint64_t)a.kv_block_stride;
+    const int tpb_mask = (1 << tpb_shift) - 1;
     auto fill_window = [&](int start) {
-      for (int i = threadIdx.x; i < kTableWindow; i += NTHREADS)
-        tbl_lds[i] = start + i < nblk ? table[b0 + start + i] : 0;
+      for (int i = threadIdx.x; i < kTableWindow; i += NTHREADS) {
+        const int ua = tile0 + min(start + i, ntiles - 1);
+        toff_lds[i] = (uint64_t)(uint32_t)table[ua >> tpb_shift] * bstride64 +
+                      (uint32_t)((ua & tpb_mask) * (16 * D * ES));
+      }
     };
-    auto rel_block = [&](int u) { return ((tile0 + min(u, ntiles - 1)) >> tpb_shift) - b0; };
-    int win0 = 0;
+    int win0 = 0;  // first tile of the window
     fill_window(0);
     __syncthreads();
 
     char* ring = work_lds + tg * (kRing * KT * kStageBytes);
-    const bool issuer = tile == 0;
+    const bool copier = tile == 0;
+    constexpr int kCopyTransfers = NKL * KPiece::kTransfers + kVBytes / 1024;  // per tile
     // ring slots hold KT consecutive tiles: step unit us covers tiles
     // us KT .. us KT + KT - 1 (those past the partition read nothing).
-    // Their block ids come from the window; the issuer reads the next step's
-    // ids right after its copy (their LDS round trip then hides behind the
-    // step instead of queueing behind every wave's tile reads), except across
-    // a window refill.  An id outside the window is clamped into it and only
-    // ever used for a step that refills first (and reads its ids again).
-    auto window_ids = [&](int us, int* blk) {
+    // The copier reads the next step's offsets right after its copy (their LDS
+    // round trip then hides behind the step), except across a window refill.
+    // An offset outside the window is clamped into it and only ever used for
+    // a step that refills first (and reads its offsets again).
+    auto window_offs = [&](int us, uint64_t* o) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
-        blk[kt] = tbl_lds[min(max(rel_block(us * KT + kt) - win0, 0), kTableWindow - 1)];
+        o[kt] = toff_lds[min(min(us * KT + kt, ntiles - 1) - win0, kTableWindow - 1)];
     };
-    auto copy = [&](int us, int slot, const int* ids) {
+    auto copy = [&](int us, int slot, const uint64_t* offs) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         const int u = us * KT + kt;
         const int ua = tile0 + u;
-        const int blk = __builtin_amdgcn_readfirstlane(ids[kt]);
-        const size_t off = (size_t)blk * bstride + (size_t)(ua & ((1 << tpb_shift) - 1)) * (16 * D * ES);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)offs[kt]);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(offs[kt] >> 32));
+        const uint64_t off = ((uint64_t)hi << 32) | lo;
         const uint32_t bytes = u < ntiles ? (uint32_t)min(tok1 - ua * TT, TT) * (D * ES) : 0u;
+        char* dst = ring + (slot * KT + kt) * kStageBytes;
         const rsrc_t rk = make_rsrc(kbase + off, bytes);
         const rsrc_t rv = make_rsrc(vbase + off, bytes);
-        char* dst = ring + (slot * KT + kt) * kStageBytes;
 #pragma unroll
         for (int i = 0; i < NKL; ++i) KPiece::copy(rk, k_lane + 64u * i, dst + i * KPiece::kBytes);
         if constexpr (TRV) lds_copy_rows_swizzled(rv, dst + NKL * KPiece::kBytes, v_swz);
@@ -575,31 +584,31 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     };
     const int nunits = (ntiles + KT - 1) / KT;
     const int nsteps = (nunits + TG - 1) / TG;
-    int ids[KT];
-    if (issuer) {
+    uint64_t offs[KT];
+    if (copier) {
 #pragma unroll
       for (int k = 0; k + 1 < kRing; ++k) {
-        window_ids(tg + k * TG, ids);
-        copy(tg + k * TG, k, ids);
+        window_offs(tg + k * TG, offs);
+        copy(tg + k * TG, k, offs);
       }
-      window_ids(tg + (kRing - 1) * TG, ids);  // step 0's
+      window_offs(tg + (kRing - 1) * TG, offs);  // step 0's
     }
     for (int j = 0; j < nsteps; ++j) {
-      if (issuer) wait_vmcnt<kTransfers * KT * (kRing - 2)>();  // unit j has landed
+      if (copier) wait_vmcnt<kCopyTransfers * KT * (kRing - 2)>();  // unit j has landed
       // the units copied in this step are (j + kRing - 1) TG + 0 .. TG - 1
       const int first = (j + kRing - 1) * TG;
-      const bool refill = rel_block((first + TG) * KT - 1) >= win0 + kTableWindow;  // same for every wave
+      const bool refill = min((first + TG) * KT, ntiles) - 1 - win0 >= kTableWindow;  // same for every wave
       if (refill) {
-        lds_barrier();  // every issuer is done with the old window
-        win0 = rel_block(first * KT);
+        lds_barrier();  // every copier is done with the old window
+        win0 = first * KT;
         fill_window(win0);
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       }
       lds_barrier();  // unit j is visible to every wave; slot (j - 1) % kRing is free
-      if (issuer) {
-        if (refill) window_ids(tg + first, ids);
-        copy(tg + first, (j + kRing - 1) % kRing, ids);
-        window_ids(tg + first + TG, ids);  // the next step's
+      if (copier) {
+        if (refill) window_offs(tg + first, offs);
+        copy(tg + first, (j + kRing - 1) % kRing, offs);
+        window_offs(tg + first + TG, offs);  // the next step's
       }
       const int uc = tg + j * TG;
       if (uc < nunits) {
@@ -609,7 +618,7 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
         process(T, uc * KT, ring + (j % kRing) * KT * kStageBytes + NKL * KPiece::kBytes);
       }
     }
-    if (issuer) wait_vmcnt<0>();  // the copies past the end have landed before the LDS is reused
+    if (copier) wait_vmcnt<0>();  // the copies past the end have landed before the LDS is reused
   }
 
   // ---- complete the per-lane sums over the 4 lane groups -------------------

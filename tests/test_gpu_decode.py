@@ -329,9 +329,10 @@ def test_fp8_mqa_workload_full_size():
 
 # ---------------------------------------------------------------------------
 # Groups of more than 16 heads: the head-tile waves of a token group share
-# each K/V tile through an LDS ring and read block ids from an LDS window of
-# the table (512 entries), refilled as the walk moves on.  Long contexts at
-# small block sizes cross that window.
+# each K/V tile through an LDS ring and read tile source offsets from an LDS
+# window (512 tiles of 16 tokens, 8 for 8-token blocks), refilled as the walk
+# moves on.  Long contexts cross that window (4096 tokens at block size 8,
+# 8192 otherwise; at block size 64 a window entry is a quarter block).
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("group", [20, 48, 64])
@@ -340,7 +341,7 @@ def test_fp8_mqa_workload_full_size():
 def test_shared_tile_groups(group, kv, head_size):
     dev = device()
     dtype = "bf16" if head_size == 128 else "f16"
-    for block_size, lens in ((8, [1, 9, 300, 4500]), (16, [17, 1000, 8300]), (64, [63, 65, 2000])):
+    for block_size, lens in ((8, [1, 9, 300, 4500]), (16, [17, 1000, 8300]), (64, [63, 65, 2000, 8500])):
         inp = to_device(make(num_seqs=len(lens), num_heads=group, num_kv_heads=1,
                              head_size=head_size, block_size=block_size, dtype=dtype,
                              seed=group + head_size + block_size, context_lens=lens, alibi=True,

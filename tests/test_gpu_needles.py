@@ -12,8 +12,9 @@ partitions where the auto plan is a single pass):
   * the same with an FP8 E4M3 cache;
   * MQA 48/1 fp16 ragged 64..8192 with ALiBi, batch 256 (the LDS-staged path
     of groups above 16 heads, split, longest first);
-  * 8-token blocks with contexts past the 512-entry LDS window of the block
-    table that the staged path keeps (refills at 4096, 8192 ... tokens),
+  * 8-token blocks with contexts past the 512-tile LDS window of tile
+    source offsets that the staged path keeps (refills at 4096, 8192 ...
+    tokens),
     16-bit and FP8 caches, 48- and 64-head groups.
 """
 import numpy as np
@@ -86,7 +87,7 @@ def test_mqa_ragged_alibi_needles(kv):
 @pytest.mark.parametrize("group,dtype", [(48, "f16"), (64, "bf16")])
 @pytest.mark.parametrize("kv", ["native", "fp8"])
 def test_table_window_needles(group, dtype, kv):
-    """Block size 8: the staged loop's LDS window of 512 table entries covers
+    """Block size 8: the staged loop's LDS window of 512 tile offsets covers
     4096 tokens, so these contexts refill it once or more mid-walk."""
     dev = device()
     lens = [4097, 9000, 12345, 600]
