@@ -153,7 +153,8 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   static_assert(KT == 1 || (KT == 2 && STAGE), "tile pairs are staged");
   constexpr int kRing = KT == 2 ? 3 : 4;  // ring slots (of KT tiles)
   // A staged tile: K as per-lane 16-byte pieces, V as the tile's own 16 rows
-  // (contiguous in the cache), read back at the direct-load offsets.
+  // (contiguous in the cache), read back at the direct-load offsets (TRV:
+  // K, like V, as the tile's 16 rows with swizzled pieces; see below).
   //
   // TRV (staged, 16-bit caches, D = 128): the P.V operand V^T is read from
   // the ring with LDS transpose reads instead of being regrouped in
@@ -320,11 +321,20 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
   const uint32_t k_lane = (uint32_t)(r * D * ES + j * 16);         // read-0 K chunk
   const uint32_t v_lane = (uint32_t)((4 * j) * D + r * EPL) * ES;  // load-0 V slice
-  // TRV: the V source offset of this lane in LDS transfer c (rows 4 c ..
-  // 4 c + 3; the transfer's own 1 KB step comes from its immediate offset),
-  // and the transpose-read offset of output tile m in a staged V tile
-  uint32_t v_swz[TRV ? 4 : 1], v_tr[TRV ? 8 : 1];
+  // TRV: the K and V source offsets of this lane in LDS transfer c (rows
+  // 4 c .. 4 c + 3; the transfer's own 1 KB step comes from its immediate
+  // offset), the K read offset of q.K step i and the transpose-read offset of
+  // output tile m in a staged tile.  Staged K rows keep their 16-byte pieces
+  // XOR-swizzled by the row index (piece p at p ^ t): a K read's lanes (rows
+  // r, pieces 4 i + j) then never share a bank, and the tile's K takes one
+  // M0 set-up and four transfers like its V.
+  uint32_t v_swz[TRV ? 4 : 1], v_tr[TRV ? 8 : 1], k_swz[TRV ? 4 : 1], k_rd[TRV ? 4 : 1];
   if constexpr (TRV) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      k_swz[c] = (uint32_t)(j * 256 + ((r ^ (4 * c + j)) & 15) * 16);
+      k_rd[c] = (uint32_t)(r * 256 + (((4 * c + j) ^ r) & 15) * 16);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       v_swz[c] = (uint32_t)(j * 256 + ((r ^ (2 * (4 * c + j))) & 15) * 16);
@@ -566,8 +576,12 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
         char* dst = ring + (slot * KT + kt) * kStageBytes;
         const rsrc_t rk = make_rsrc(kbase + off, bytes);
         const rsrc_t rv = make_rsrc(vbase + off, bytes);
+        if constexpr (TRV) {
+          lds_copy_rows_swizzled(rk, dst, k_swz);
+        } else {
 #pragma unroll
-        for (int i = 0; i < NKL; ++i) KPiece::copy(rk, k_lane + 64u * i, dst + i * KPiece::kBytes);
+          for (int i = 0; i < NKL; ++i) KPiece::copy(rk, k_lane + 64u * i, dst + i * KPiece::kBytes);
+        }
         if constexpr (TRV) lds_copy_rows_swizzled(rv, dst + NKL * KPiece::kBytes, v_swz);
         else lds_copy_run<kVBytes>(rv, dst + NKL * KPiece::kBytes, lane);
       }
@@ -575,7 +589,10 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     auto read = [&](Tile& T, int slot, int kt) {
       const char* src = ring + (slot * KT + kt) * kStageBytes;
 #pragma unroll
-      for (int i = 0; i < NKL; ++i) KS::split(KPiece::read(src + i * KPiece::kBytes, lane), &T.k[i * KSTEP]);
+      for (int i = 0; i < NKL; ++i) {
+        if constexpr (TRV) KS::split(*reinterpret_cast<const uint4*>(src + k_rd[i]), &T.k[i * KSTEP]);
+        else KS::split(KPiece::read(src + i * KPiece::kBytes, lane), &T.k[i * KSTEP]);
+      }
       if constexpr (!TRV) {  // (TRV: P.V reads V itself, transposed)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
