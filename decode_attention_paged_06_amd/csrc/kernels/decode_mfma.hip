@@ -610,7 +610,12 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       }
       window_offs(tg + (kRing - 1) * TG, offs);  // step 0's
     }
-    for (int j = 0; j < nsteps; ++j) {
+    // One step; its ring slot is a compile-time constant (the loop below is
+    // unrolled by the ring size), so every LDS address of the tile reads is a
+    // loop-invariant lane offset plus an immediate (MQA 48/1: one address add
+    // fewer per K and V^T read).
+    auto step = [&](int j, auto slot_tag) {
+      constexpr int kSlot = decltype(slot_tag)::value;  // j % kRing
       if (copier) wait_vmcnt<kCopyTransfers * KT * (kRing - 2)>();  // unit j has landed
       // the units copied in this step are (j + kRing - 1) TG + 0 .. TG - 1
       const int first = (j + kRing - 1) * TG;
@@ -624,15 +629,24 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       lds_barrier();  // unit j is visible to every wave; slot (j - 1) % kRing is free
       if (copier) {
         if (refill) window_offs(tg + first, offs);
-        copy(tg + first, (j + kRing - 1) % kRing, offs);
+        copy(tg + first, (kSlot + kRing - 1) % kRing, offs);
         window_offs(tg + first + TG, offs);  // the next step's
       }
       const int uc = tg + j * TG;
       if (uc < nunits) {
         Tile T[KT];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) read(T[kt], j % kRing, kt);
-        process(T, uc * KT, ring + (j % kRing) * KT * kStageBytes + NKL * KPiece::kBytes);
+        for (int kt = 0; kt < KT; ++kt) read(T[kt], kSlot, kt);
+        process(T, uc * KT, ring + kSlot * KT * kStageBytes + NKL * KPiece::kBytes);
+      }
+    };
+    static_assert(kRing == 3 || kRing == 4, "the loop is unrolled by the ring size");
+    for (int j = 0; j < nsteps; j += kRing) {
+      step(j, std::integral_constant<int, 0>{});
+      if (j + 1 < nsteps) step(j + 1, std::integral_constant<int, 1>{});
+      if (j + 2 < nsteps) step(j + 2, std::integral_constant<int, 2>{});
+      if constexpr (kRing == 4) {
+        if (j + 3 < nsteps) step(j + 3, std::integral_constant<int, kRing == 4 ? 3 : 0>{});
       }
     }
     if (copier) wait_vmcnt<0>();  // the copies past the end have landed before the LDS is reused
