@@ -602,13 +602,23 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
     const int nunits = (ntiles + KT - 1) / KT;
     const int nsteps = (nunits + TG - 1) / TG;
     uint64_t offs[KT];
+    // Decode walks the partition's units last to first when the window holds
+    // all of them: with ALiBi the bias grows toward the query token, so the
+    // running max is set by the first units and the rescale of the
+    // accumulators (every unit, for the steep slopes, in ascending order) is
+    // rare (MQA 48/1 ALiBi batch 256, FP8 cache: 93.3 -> 86.8 us; 16-bit
+    // 104.6 -> 103.9 us).  Every unit of a decode partition holds a key the
+    // row sees, so the first unit sets a finite max.  Multi-query rows can
+    // see none of a late unit's keys, so they keep the ascending order.
+    const bool reverse = a.query_start == nullptr && ntiles <= kTableWindow;
+    auto order = [&](int u) { return reverse && u < nunits ? nunits - 1 - u : u; };
     if (copier) {
 #pragma unroll
       for (int k = 0; k + 1 < kRing; ++k) {
-        window_offs(tg + k * TG, offs);
-        copy(tg + k * TG, k, offs);
+        window_offs(order(tg + k * TG), offs);
+        copy(order(tg + k * TG), k, offs);
       }
-      window_offs(tg + (kRing - 1) * TG, offs);  // step 0's
+      window_offs(order(tg + (kRing - 1) * TG), offs);  // step 0's
     }
     // One step; its ring slot is a compile-time constant (the loop below is
     // unrolled by the ring size), so every LDS address of the tile reads is a
@@ -628,16 +638,16 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       }
       lds_barrier();  // unit j is visible to every wave; slot (j - 1) % kRing is free
       if (copier) {
-        if (refill) window_offs(tg + first, offs);
-        copy(tg + first, (kSlot + kRing - 1) % kRing, offs);
-        window_offs(tg + first + TG, offs);  // the next step's
+        if (refill) window_offs(order(tg + first), offs);
+        copy(order(tg + first), (kSlot + kRing - 1) % kRing, offs);
+        window_offs(order(tg + first + TG), offs);  // the next step's
       }
       const int uc = tg + j * TG;
       if (uc < nunits) {
         Tile T[KT];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) read(T[kt], kSlot, kt);
-        process(T, uc * KT, ring + kSlot * KT * kStageBytes + NKL * KPiece::kBytes);
+        process(T, order(uc) * KT, ring + kSlot * KT * kStageBytes + NKL * KPiece::kBytes);
       }
     };
     static_assert(kRing == 3 || kRing == 4, "the loop is unrolled by the ring size");
