@@ -32,6 +32,13 @@ constexpr float kPosBig = 1.0e30f;
 __device__ __forceinline__ float score_max(float a, float b) {
   return __builtin_amdgcn_fmed3f(a, b, kPosBig);
 }
+// Maximum of three logits, one v_max3_f32 (the compiler would quiet each
+// input of an fmaxf chain first).
+__device__ __forceinline__ float score_max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // ---- 16-bit storage formats -------------------------------------------------
 
