@@ -650,7 +650,12 @@ def main():
     ceiling = None
     if not a.no_ceiling:
         try:
-            ceiling = device_ceiling()
+            # scattered runs the size of the workload's contiguous cache run: one
+            # (block, kv head) tile of K and V in the joint layout, of K or V alone
+            # in separate tensors (1 byte per element for an FP8 cache)
+            elem = 1 if args.get("kv_dtype") == "fp8" else 2
+            run = args["block_size"] * args["head_size"] * elem * (2 if a.kv_layout == "joint" else 1)
+            ceiling = device_ceiling(run_bytes=max(1024, 1 << (run.bit_length() - 1)))
         except torch.cuda.OutOfMemoryError as e:  # context only: never fail the bench for it
             ceiling = {"error": f"not measured: {e.__class__.__name__}"}
             torch.cuda.empty_cache()
