@@ -436,9 +436,10 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       // exceeds it by more than kRescaleSlack (weights then stay below
       // 2^kRescaleSlack): the rescale of l and the accumulators is rare, and
       // the result is the same quotient acc / l whichever m it is taken against.
-      const float mx = column_max4(local);
-      if (wave_any(mx > m[rt] + kRescaleSlack)) {
-        const float mn = score_max(m[rt], mx);
+      // Each lane tests its own keys; only a step that moves m takes the row
+      // max across the four lane groups, so all four move m alike.
+      if (wave_any(local > m[rt] + kRescaleSlack)) {
+        const float mn = score_max(m[rt], column_max4(local));
         const float alpha = fast_exp2(m[rt] - mn);
         m[rt] = mn;
         lsum[rt] *= alpha;

@@ -288,10 +288,11 @@ __global__ __launch_bounds__(kW * 64) void prefill_mfma32_kernel(const DecodeArg
     const float t0 = score_max3(sc[0], sc[1], sc[2]), t1 = score_max3(sc[3], sc[4], sc[5]);
     const float t2 = score_max3(sc[6], sc[7], sc[8]), t3 = score_max3(sc[9], sc[10], sc[11]);
     const float t4 = score_max3(sc[12], sc[13], sc[14]);
-    float mx = score_max(score_max3(t0, t1, t2), score_max3(t3, t4, sc[15]));
-    mx = xor32_pair_max(mx * xs);
-    if (wave_any(mx > m + kRescaleSlack)) {
-      const float mn = score_max(m, mx);
+    // (this lane's half of the row: the other half, lane n + 32, is consulted
+    // only by a step that moves m, so both halves move it alike)
+    const float local = xs * score_max(score_max3(t0, t1, t2), score_max3(t3, t4, sc[15]));
+    if (wave_any(local > m + kRescaleSlack)) {
+      const float mn = score_max(m, xor32_pair_max(local));
       const float alpha = fast_exp2(m - mn);
       m = mn;
       lsum *= alpha;
