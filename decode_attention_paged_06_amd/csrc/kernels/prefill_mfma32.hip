@@ -10,15 +10,17 @@
 // (sequence, kv head) -- row i G + g is new token i, query head g of the
 // group -- and walks the keys they see in steps of 32 (two 16-row cache
 // tiles), staged once per step through an LDS ring of three slots that all
-// four waves fill (a quarter each) and read.  Wave w owns rows 32 w .. 32 w + 31 and computes, per step,
+// four waves fill (a quarter each) and read.  Wave w owns rows 32 w ..
+// 32 w + 31 and computes, per step,
 //   S^T[key, row]  = sum_d K[key, d] Q[row, d]     8 x v_mfma_f32_32x32x16 (D / 16)
 //   O^T[d, row]   += sum_key V[key, d] P[row, key]  8 x v_mfma_f32_32x32x16 (4 d-blocks x 2)
 // Register layouts (lane = 32 jj + n):
 //   Q operand, k-step s : Q[row n][dims 16 s + 8 jj .. + 7]   (in registers all along)
 //   K operand, k-step s : K[key n][dims 16 s + 8 jj .. + 7]   (from LDS)
 //   S^T, register r     : key 8 (r / 4) + 4 jj + r % 4, row n -- so a lane holds
-//                         16 keys of one row, and the row maximum is 15
-//                         in-lane maxima and one lane swap (lanes n, n + 32)
+//                         16 keys of one row (half of them; lane n + 32 has
+//                         the rest), and its maximum is a tree of in-lane
+//                         three-input maxima
 //   P operand, half h   : the lane's S registers 8 h .. 8 h + 7 as weights, i.e.
 //                         keys 16 h + 8 e' + 4 jj + v (e' = 0, 1; v = 0..3)
 //   V^T operand, block b, half h : V[those keys][dims 32 b + n], taken with two
@@ -37,8 +39,10 @@
 //
 // Softmax: fp32 online softmax in log2 units against a per-row reference max
 // that moves only when a step's max exceeds it by more than 8 (weights stay
-// below 2^8, the rescale is rare); P is rounded to the 16-bit type for the
-// matrix product and l sums the same rounded weights.  Built for 16-bit
+// below 2^8, the rescale is rare; each lane tests its own half of the row,
+// and the two halves are combined only on a step that moves the max); P is
+// rounded to the 16-bit type for the matrix product and l sums the same
+// rounded weights.  Built for 16-bit
 // caches, head size 128 and cache blocks of at least 16 tokens; other
 // multi-query calls run on the general kernel.
 #include <type_traits>
