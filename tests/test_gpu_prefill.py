@@ -163,3 +163,24 @@ def test_prefill32_window_refill(BS):
     ref = ref_prefill(inp, q, qs)
     for ps in (-1, 0):
         compare(run_prefill(inp, q, qs, max_q, ps), ref, "bf16", what=f"refill BS={BS} partition={ps}")
+
+
+def test_prefill32_full_causal_sampled():
+    """One sequence whose whole 4096-token context is new (a full causal
+    prefill: 256 row chunks per kv head, up to 128 steps each, longest chunks
+    first), on the 32 x 32 kernel under the automatic plan; sampled rows are
+    checked through the fp64 decode oracle on the context cut at each row's
+    position."""
+    dev = device()
+    L = n = 4096
+    inp, q, qs, max_q = prefill_inputs(new_tokens=[n], seed=4096, device=dev, num_seqs=1,
+                                       num_heads=64, num_kv_heads=8, head_size=128,
+                                       block_size=16, dtype="bf16", context_lens=L, alibi=True)
+    out = run_prefill(inp, q, qs, max_q)
+    rows = [0, 1, 15, 16, 31, 32, 127, 128, 2047, 2048, 4094, 4095]
+    tables = inp.block_tables.cpu().numpy()[[0] * len(rows)]
+    lens = np.array([r + 1 for r in rows], dtype=np.int64)
+    ref = oracle.paged_decode(raw_u16(q[rows]), raw_bits(inp.key_cache), raw_bits(inp.value_cache),
+                              tables, lens, inp.scale, inp.block_size, inp.alibi_slopes.cpu().numpy(),
+                              dtype="bf16", k_scale=inp.k_scale, v_scale=inp.v_scale)
+    compare(out[rows], ref, "bf16", what="full causal prefill 4096, sampled rows")
