@@ -133,6 +133,7 @@ P32_CASES = [
     ("p32-bs32-f16", 32, 4, "f16", 32, [513, 64], [200, 64], False),
     ("p32-bs256", 8, 1, "bf16", 256, [700, 2100], [150, 33], True),
     ("p32-mqa48", 48, 1, "bf16", 16, [400, 45], [100, 45], True),
+    ("p32-g12-f16-bs128-alibi", 24, 2, "f16", 128, [1500, 257, 3000], [400, 257, 64], True),
 ]
 
 
