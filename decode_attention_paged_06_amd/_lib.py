@@ -15,7 +15,7 @@ PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_KV_NATIVE, PA_KV_FP8_E4M3 = 0, 1
 PA_KV_SEPARATE, PA_KV_JOINT = 0, 1
 PA_ENGINE_AUTO, PA_ENGINE_VALU, PA_ENGINE_MFMA = 0, 1, 2
-PA_SCHEDULE_AUTO, PA_SCHEDULE_GRID, PA_SCHEDULE_LONGEST_FIRST = 0, 1, 2
+PA_SCHEDULE_AUTO, PA_SCHEDULE_GRID, PA_SCHEDULE_LONGEST_FIRST, PA_SCHEDULE_EQUAL_SHARES = 0, 1, 2, 3
 # PA_NOALLOC_SCRATCH_BYTES of include/paged_attention.h
 NOALLOC_SCRATCH_BYTES = 32 << 20
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_ALIGNMENT",
@@ -26,8 +26,8 @@ EXPORTS = ("paged_attention_decode", "paged_attention_decode_noalloc", "paged_at
            "paged_attention_prefill", "paged_attention_prefill_workspace_bytes",
            "paged_attention_prefill_plan", "gather_cached_kv", "paged_kv_cache_write",
            "pa_status_string", "pa_last_error")
-# The measurement aid of csrc/measure.h (exported, not part of the public header).
-MEASURE_EXPORTS = ("pa_stream_read_probe", "pa_stream_read_sink_bytes")
+# The measurement aids of csrc/measure.h (exported, not part of the public header).
+MEASURE_EXPORTS = ("pa_stream_read_probe", "pa_stream_read_sink_bytes", "pa_share_occupancy")
 
 
 class PaDims(ctypes.Structure):
@@ -97,6 +97,9 @@ def lib() -> ctypes.CDLL:
     L.pa_stream_read_probe.restype = ctypes.c_int
     L.pa_stream_read_sink_bytes.argtypes = [sz]
     L.pa_stream_read_sink_bytes.restype = sz
+    L.pa_share_occupancy.argtypes = [ctypes.POINTER(PaDims), ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                     ctypes.POINTER(i32)]
+    L.pa_share_occupancy.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_last_error.argtypes = []

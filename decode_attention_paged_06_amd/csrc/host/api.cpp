@@ -168,6 +168,56 @@ size_t split_workspace(const pa_dims* d, const CallShape& c, int P, bool longest
   return split_layout(d, c, P, longest_first).bytes;
 }
 
+// Workspace of an equal-share decode plan with `wgs` workgroups: fp32 partial
+// outputs [group head][slots][D], then (m, l) pairs [group head][slots], then
+// the tile prefix over sequences (num_seqs + 1 ints).  A piece of item i
+// (kv head * num_seqs + sequence) walked by workgroup b sits in slot i + b.
+struct SharesLayout {
+  size_t ml_offset = 0, pfx_offset = 0, bytes = 0;
+  int64_t slots = 0;
+};
+SharesLayout shares_layout(const pa_dims* d, int wgs) {
+  SharesLayout w;
+  const size_t group = (size_t)(d->num_heads / d->num_kv_heads);
+  w.slots = (int64_t)d->num_seqs * d->num_kv_heads + wgs;
+  w.ml_offset = align_up((size_t)w.slots * group * d->head_size * sizeof(float), kWsAlign);
+  w.pfx_offset = align_up(w.ml_offset + (size_t)w.slots * group * 2 * sizeof(float), kWsAlign);
+  w.bytes = w.pfx_offset + ((size_t)d->num_seqs + 1) * sizeof(int32_t);
+  return w;
+}
+
+// Equal shares apply to decode on the staged kernel (groups of more than 16
+// heads) for batches whose tile prefix fits the kernel's LDS and int32.
+bool shares_fit(const pa_dims* d, const CallShape& c, int engine) {
+  const int group = d->num_heads / d->num_kv_heads;
+  const int64_t tiles = ((int64_t)d->max_blocks_per_seq * d->block_size + 15) / (d->block_size < 16 ? d->block_size : 16);
+  return engine == PA_ENGINE_MFMA && !c.multi && pa::mfma_head_tiles(group) > 1 &&
+         d->num_seqs <= pa::kStreamMaxSeqs && (int64_t)d->num_seqs * tiles < ((int64_t)1 << 31);
+}
+
+// Workgroups of the equal-share kernel one CU holds on the current device
+// (the runtime's occupancy of the compiled kernel; looked up once per device
+// and configuration), at most what its LDS allows.
+std::atomic<int> g_share_occ[kMaxDevices][2][2][3][2];
+int share_occupancy(const pa_dims* d, int* out) {
+  const int group = d->num_heads / d->num_kv_heads;
+  const bool fp8 = d->kv_format == PA_KV_FP8_E4M3;
+  const int bound = pa::staged_decode_wgs_per_cu(d->head_size, group, fp8);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_DEVICE, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_DEVICE, "device index %d", dev);
+  std::atomic<int>& slot = g_share_occ[dev][d->dtype == PA_BF16][d->head_size == 128]
+                                      [pa::mfma_head_tiles(group) - 2][fp8];
+  int n = slot.load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (pa::staged_decode_occupancy(d->dtype == PA_BF16 ? 1 : 0, d->head_size, group, fp8, &n) != hipSuccess || n <= 0)
+      return fail(PA_ERR_DEVICE, "cannot query the occupancy of the decode kernel on device %d", dev);
+    slot.store(n, std::memory_order_relaxed);
+  }
+  *out = n < bound ? n : bound;
+  return PA_OK;
+}
+
 int resolve_engine(const pa_dims* d, const CallShape& c, const pa_opts* o, int* engine) {
   int e = o ? o->engine : PA_ENGINE_AUTO;
   if (e != PA_ENGINE_AUTO && e != PA_ENGINE_VALU && e != PA_ENGINE_MFMA)
@@ -209,15 +259,16 @@ int make_plan(const pa_dims* d, const CallShape& c, size_t ws_bytes, const pa_op
   const int group = d->num_heads / d->num_kv_heads;
   const int schedule = o ? o->schedule : PA_SCHEDULE_AUTO;
   if (schedule != PA_SCHEDULE_AUTO && schedule != PA_SCHEDULE_GRID &&
-      schedule != PA_SCHEDULE_LONGEST_FIRST)
+      schedule != PA_SCHEDULE_LONGEST_FIRST && schedule != PA_SCHEDULE_EQUAL_SHARES)
     return fail(PA_ERR_INVALID_ARG, "schedule %d", schedule);
   // Longest-first ordering applies to split decode plans on the MFMA engine;
-  // automatic for groups of more than 16 heads (48-head MQA with ragged
-  // lengths measured faster), on request otherwise.
+  // automatic for groups of more than 16 heads that do not take equal shares,
+  // on request otherwise.
   const bool longest_first =
       engine == PA_ENGINE_MFMA && !c.multi &&
       (schedule == PA_SCHEDULE_LONGEST_FIRST ||
-       (schedule == PA_SCHEDULE_AUTO && pa::mfma_head_tiles(group) > 1));
+       ((schedule == PA_SCHEDULE_AUTO || schedule == PA_SCHEDULE_EQUAL_SHARES) &&
+        pa::mfma_head_tiles(group) > 1));
   int P = 1, PB = maxb;
 
   if (forced == -1) {
@@ -245,7 +296,35 @@ int make_plan(const pa_dims* d, const CallShape& c, size_t ws_bytes, const pa_op
                                                                    : kTargetGroupsPerCu) * cus;
     const int min_tokens = one_tile && !fp8 ? kMinPartitionTokensOneTile : kMinPartitionTokens;
     const int min_pb = min_tokens / d->block_size > 1 ? min_tokens / d->block_size : 1;
-    if (units > 0 && units < target && maxb > min_pb) {
+    const bool split = units > 0 && units < target && maxb > min_pb;
+    // Equal shares (groups of more than 16 heads, on request, or where the
+    // auto plan would split a batch of fewer (kv head, sequence) items than
+    // the CUs hold workgroups): as many workgroups as the CUs hold at once,
+    // each walking an equal share of the batch's tiles.  With at least as
+    // many items as workgroup slots every slot starts on a whole item and
+    // longest-first partitions balance the rest without cutting items at
+    // arbitrary tiles.  Measured, ragged 64..8192 ALiBi batches, graph
+    // replay, longest first -> equal shares: 48-head groups batch 32 35.7 ->
+    // 28.7 us; 32-head groups batch 64 41.2 -> 38.9 us, batch 256 112.8 ->
+    // 109.4 us; 64-head groups batch 256 140.5 -> 125.7 us (FP8 138.3 ->
+    // 107.7); but 48-head groups at batch 256 (256 items, one workgroup per
+    // CU) 104 -> 109.5 us, so these keep partitions.
+    const int wgs_per_cu = pa::staged_decode_wgs_per_cu(d->head_size, group, fp8);
+    if (shares_fit(d, c, engine) &&
+        (schedule == PA_SCHEDULE_EQUAL_SHARES ||
+         (schedule == PA_SCHEDULE_AUTO && split && units < (long long)cus * wgs_per_cu))) {
+      const int wgs = cus * wgs_per_cu;
+      const size_t need = shares_layout(d, wgs).bytes;
+      if (unlimited || need <= ws_bytes) {
+        p->num_partitions = wgs;
+        p->partition_size = 0;
+        p->engine = engine;
+        p->schedule = PA_SCHEDULE_EQUAL_SHARES;
+        p->workspace_bytes = need;
+        return PA_OK;
+      }
+    }
+    if (split) {
       long long want = (target + units - 1) / units;
       PB = (int)((maxb + want - 1) / want);
       if (PB < min_pb) PB = min_pb;
@@ -312,7 +391,8 @@ int run_attention(void* out, const void* query, const void* key_cache, const voi
 
   pa_plan plan;
   if ((st = make_plan(dims, c, workspace ? workspace_bytes : 0, opts, false, &plan))) return st;
-  if (plan.num_partitions > 1) {
+  const bool shares = plan.schedule == PA_SCHEDULE_EQUAL_SHARES;
+  if (plan.num_partitions > 1 || shares) {
     if (!workspace) return fail(PA_ERR_WORKSPACE, "split plan needs a workspace");
     if (!aligned(workspace, kWsAlign))
       return fail(PA_ERR_ALIGNMENT, "workspace must be %zu-byte aligned", kWsAlign);
@@ -348,7 +428,20 @@ int run_attention(void* out, const void* query, const void* key_cache, const voi
   a.unit_order = nullptr;
   const bool longest_first = plan.schedule == PA_SCHEDULE_LONGEST_FIRST;
   int32_t* order = nullptr;
-  if (plan.num_partitions > 1) {
+  if (shares) {
+    // launched: the CUs the plan counted times what one CU holds of this kernel
+    int occ = 0;
+    if ((st = share_occupancy(dims, &occ))) return st;
+    const SharesLayout w = shares_layout(dims, plan.num_partitions);
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.ml_offset);
+    a.ws_pfx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + w.pfx_offset);
+    a.num_slots = (int32_t)w.slots;
+    const int group = dims->num_heads / dims->num_kv_heads;
+    a.stream_wgs = plan.num_partitions / pa::staged_decode_wgs_per_cu(dims->head_size, group, kv_fp8) * occ;
+    a.piece_cost = pa::staged_piece_cost(occ, kv_fp8);
+    a.num_partitions = 1;
+  } else if (plan.num_partitions > 1) {
     const SplitLayout w = split_layout(dims, c, plan.num_partitions, longest_first);
     a.ws_o = static_cast<float*>(workspace);
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.ml_offset);
@@ -371,7 +464,7 @@ int run_attention(void* out, const void* query, const void* key_cache, const voi
           ? pa::launch_prefill_mfma32(a, dims->dtype, s)
           : pa::launch_decode_mfma(a, dims->dtype, dims->head_size, kv_fp8, s);
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "attention launch: %s", hipGetErrorString(e));
-  if (plan.num_partitions > 1) {
+  if (plan.num_partitions > 1 || shares) {
     e = pa::launch_partition_reduce(a, dims->dtype, dims->head_size, s);
     if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reduce launch: %s", hipGetErrorString(e));
   }
@@ -570,6 +663,26 @@ int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
 }
 
 size_t pa_stream_read_sink_bytes(size_t bytes) { return (size_t)pa::stream_read_grid(bytes) * 16; }
+
+int pa_share_occupancy(const pa_dims* dims, int32_t* table_wgs, int32_t* device_wgs,
+                       int32_t* piece_cost) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!table_wgs || !device_wgs || !piece_cost) return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  CallShape c = decode_shape(dims);
+  if (!shares_fit(dims, c, PA_ENGINE_MFMA))
+    return fail(PA_ERR_INVALID_ARG, "these dims do not take equal shares");
+  const int group = dims->num_heads / dims->num_kv_heads;
+  const bool fp8 = dims->kv_format == PA_KV_FP8_E4M3;
+  int n = 0;
+  if (pa::staged_decode_occupancy(dims->dtype == PA_BF16 ? 1 : 0, dims->head_size, group, fp8, &n) !=
+      hipSuccess)
+    return fail(PA_ERR_DEVICE, "occupancy query failed");
+  *table_wgs = pa::staged_decode_wgs_per_cu(dims->head_size, group, fp8);
+  *device_wgs = n;
+  *piece_cost = pa::staged_piece_cost(n < *table_wgs ? n : *table_wgs, fp8);
+  return ok();
+}
 
 int pa_stream_read_probe(const void* src, size_t bytes, size_t run_bytes, void* sink,
                          size_t sink_bytes, pa_stream_t stream) {

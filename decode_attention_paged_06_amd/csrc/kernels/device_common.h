@@ -139,6 +139,17 @@ __device__ __forceinline__ float column_sum4(float x) {
 // True if any lane of the wave has `p` set.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// Inclusive prefix sum over the 64 lanes of a wave: lane i gets x_0 + .. + x_i.
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+  const int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 // ---- loads --------------------------------------------------------------------
 
 // Streaming loads of K/V: every byte is read exactly once per call, so these

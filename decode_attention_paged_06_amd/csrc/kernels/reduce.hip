@@ -12,7 +12,9 @@
 // over the partitions that hold keys the row sees (p < ceil(visible /
 // partition_size), visible = L_s for decode, position + 1 for a new token of a
 // multi-query call).  A row with a single such partition was written by the
-// decode kernel itself and is skipped here.  One wave per (head, sequence, new
+// decode kernel itself and is skipped here.  Under the equal-share schedule
+// the pieces of an item (kv head, sequence) that several decode workgroups
+// walked take the place of the partitions.  One wave per (head, sequence, new
 // token).  The (m_p,
 // l_p) pairs are read one partition per lane (64 at a time) and reduced across
 // the wave; the partial outputs are read in batches whose loads are all in
@@ -87,6 +89,18 @@ __device__ __forceinline__ void weighted_sum(const float2* ml, const Part* o, in
   }
 }
 
+// The merged row: the weighted sum over the lanes' partial weight sums.
+template <typename Fmt, int PER>
+__device__ __forceinline__ void store_row(uint16_t* orow, float wsum, float acc0, float acc1) {
+  wsum = wave_sum(wsum);
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if constexpr (PER == 2) {
+    *reinterpret_cast<uint32_t*>(orow) = Fmt::pack(acc0 * inv, acc1 * inv);
+  } else {
+    *orow = (uint16_t)(Fmt::pack(acc0 * inv, 0.f) & 0xffffu);
+  }
+}
+
 template <typename Fmt, int D>
 __global__ __launch_bounds__(64) void partition_reduce_kernel(const DecodeArgs a) {
   constexpr int PER = D / 64;
@@ -104,6 +118,39 @@ __global__ __launch_bounds__(64) void partition_reduce_kernel(const DecodeArgs a
   if (i >= n_new) return;
   const size_t row = (size_t)(q_first + i) * a.num_heads + h;
   uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + row * D + lane * PER;
+
+  if (a.stream_wgs > 0) {
+    // Equal shares: item kvh * S + seq has its tiles at stream positions
+    // [x0, x0 + n) (after its piece_cost positions); the workgroups whose
+    // shares meet them left their partials in consecutive slots item + b,
+    // b = owner(x0) .. owner(x0 + n - 1).
+    const int S = a.num_seqs;
+    const int kvh = h / a.group;
+    const int g = h - kvh * a.group;
+    const int64_t cost = a.piece_cost;
+    const int p0 = a.ws_pfx[seq], n = a.ws_pfx[seq + 1] - p0;
+    const int64_t T1 = a.ws_pfx[S] + cost * S;
+    if (n <= 0) {  // no context: zero output row
+      if constexpr (PER == 2) *reinterpret_cast<uint32_t*>(orow) = 0u;
+      else *orow = 0;
+      return;
+    }
+    const int64_t T = T1 * a.num_kv_heads;
+    const int64_t nwg = T < a.stream_wgs ? T : a.stream_wgs;  // workgroups with a share
+    const int64_t x0 = kvh * T1 + p0 + cost * (seq + 1);
+    const int bf = (int)stream_owner(x0, T, nwg);
+    const int nact = (int)stream_owner(x0 + n - 1, T, nwg) - bf + 1;
+    if (nact == 1) return;  // one workgroup held the whole item and wrote this row
+    const size_t first = (size_t)g * a.num_slots + (size_t)kvh * S + seq + bf;
+    const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + first;
+    const Part* o = reinterpret_cast<const Part*>(a.ws_o + first * D) + lane;
+    float wsum = 0.f, acc0 = 0.f, acc1 = 0.f;
+    if (nact <= 4) weighted_sum<4>(ml, o, nact, D / PER, lane, wsum, acc0, acc1);
+    else if (nact <= 8) weighted_sum<8>(ml, o, nact, D / PER, lane, wsum, acc0, acc1);
+    else weighted_sum<16>(ml, o, nact, D / PER, lane, wsum, acc0, acc1);
+    store_row<Fmt, PER>(orow, wsum, acc0, acc1);
+    return;
+  }
 
   const int L = min(a.context_lens[seq], a.max_blocks_per_seq * a.block_size);
   if (L <= 0) {
@@ -123,13 +170,7 @@ __global__ __launch_bounds__(64) void partition_reduce_kernel(const DecodeArgs a
   if (nact <= 4) weighted_sum<4>(ml, o, nact, D / PER, lane, wsum, acc0, acc1);
   else if (nact <= 8) weighted_sum<8>(ml, o, nact, D / PER, lane, wsum, acc0, acc1);
   else weighted_sum<16>(ml, o, nact, D / PER, lane, wsum, acc0, acc1);
-  wsum = wave_sum(wsum);
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(orow) = Fmt::pack(acc0 * inv, acc1 * inv);
-  } else {
-    *orow = (uint16_t)(Fmt::pack(acc0 * inv, 0.f) & 0xffffu);
-  }
+  store_row<Fmt, PER>(orow, wsum, acc0, acc1);
 }
 
 hipError_t launch_partition_reduce(const DecodeArgs& a, int dtype, int head_size, hipStream_t s) {

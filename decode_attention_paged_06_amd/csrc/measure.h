@@ -1,13 +1,14 @@
 /*
- * Measurement aid exported by libpagedattn.so beside the public C ABI of
- * include/paged_attention.h, for the benchmark only: not part of the
- * attention path and not installed with the public header.  Status codes and
- * pa_last_error() are the public ones.
+ * Measurement aids exported by libpagedattn.so beside the public C ABI of
+ * include/paged_attention.h, for the benchmark and the tests only: not part
+ * of the attention path and not installed with the public header.  Status
+ * codes and pa_last_error() are the public ones.
  */
 #ifndef PAGED_ATTENTION_MEASURE_H
 #define PAGED_ATTENTION_MEASURE_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #include "paged_attention.h"
 
@@ -37,6 +38,18 @@ extern "C" {
 int pa_stream_read_probe(const void* src, size_t bytes, size_t run_bytes, void* sink,
                          size_t sink_bytes, pa_stream_t stream);
 size_t pa_stream_read_sink_bytes(size_t bytes);
+
+/*
+ * pa_share_occupancy -- for the equal-share schedule of the decode call with
+ * these dims: *table_wgs = workgroups per CU the planner assumes (from the
+ * kernel's LDS), *device_wgs = what the runtime's occupancy calculator
+ * reports for the compiled kernel on the current device (needs a device),
+ * *piece_cost = the stream positions each (kv head, sequence) item takes
+ * before its tiles in the call's shares.  Returns PA_OK, PA_ERR_INVALID_ARG
+ * (dims without equal shares) or PA_ERR_DEVICE.
+ */
+int pa_share_occupancy(const pa_dims* dims, int32_t* table_wgs, int32_t* device_wgs,
+                       int32_t* piece_cost);
 
 #ifdef __cplusplus
 }

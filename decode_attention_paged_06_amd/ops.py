@@ -13,13 +13,13 @@ import torch
 from . import _lib
 from ._lib import (PA_BF16, PA_ENGINE_AUTO, PA_ENGINE_MFMA, PA_ENGINE_VALU, PA_F16, PA_FP8_E4M3,
                    PA_KV_FP8_E4M3, PA_KV_JOINT, PA_KV_NATIVE, PA_KV_SEPARATE, PA_SCHEDULE_AUTO,
-                   PA_SCHEDULE_GRID,
+                   PA_SCHEDULE_EQUAL_SHARES, PA_SCHEDULE_GRID,
                    PA_SCHEDULE_LONGEST_FIRST, PaDims, PaOpts, PaPlan, check, lib)
 
 _DTYPE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_FP8_E4M3}
 _ENGINE = {"auto": PA_ENGINE_AUTO, "valu": PA_ENGINE_VALU, "mfma": PA_ENGINE_MFMA}
 _SCHEDULE = {"auto": PA_SCHEDULE_AUTO, "grid": PA_SCHEDULE_GRID,
-             "longest_first": PA_SCHEDULE_LONGEST_FIRST}
+             "longest_first": PA_SCHEDULE_LONGEST_FIRST, "equal_shares": PA_SCHEDULE_EQUAL_SHARES}
 
 
 def joint_kv_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_size: int,
@@ -338,6 +338,16 @@ def stream_read_probe(src: torch.Tensor, sink: Optional[torch.Tensor] = None, st
     return sink
 
 
+def share_occupancy(dims: PaDims):
+    """(workgroups per CU the planner assumes, what the device's occupancy
+    calculator reports, the piece cost in stream positions) for the
+    equal-share decode kernel of these dims (a measurement aid; see
+    pa_share_occupancy)."""
+    t, d, c = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    check(lib().pa_share_occupancy(ctypes.byref(dims), ctypes.byref(t), ctypes.byref(d), ctypes.byref(c)))
+    return t.value, d.value, c.value
+
+
 __all__ = ["paged_attention_decode", "paged_attention_decode_noalloc", "paged_attention_plan", "paged_attention_workspace_bytes",
            "paged_attention_prefill", "make_prefill_dims", "gather_cached_kv", "paged_kv_cache_write",
-           "make_dims", "make_opts", "joint_kv_cache", "kv_layout_of", "stream_read_probe", "_lib"]
+           "make_dims", "make_opts", "joint_kv_cache", "kv_layout_of", "stream_read_probe", "share_occupancy", "_lib"]

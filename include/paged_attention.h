@@ -126,15 +126,27 @@ typedef enum {
   PA_ENGINE_MFMA = 2  /* matrix cores: the query group as a 16-wide MFMA tile           */
 } pa_engine;
 
-/* Order in which the work units (sequence, partition) of a split decode plan
- * on the matrix-core engine are started.  With ragged context lengths the
- * units differ in size; starting the longest first (a small ordering kernel
- * runs before the decode kernel) shortens the tail of the launch.  Results
- * are identical either way. */
+/* How a decode call that splits the context on the matrix-core engine lays
+ * its work out over workgroups.  GRID and LONGEST_FIRST cut each sequence into
+ * fixed partitions, one workgroup each; with ragged context lengths these
+ * units differ in size, and starting the longest first (a small ordering
+ * kernel runs before the decode kernel) shortens the tail of the launch.
+ * GRID and LONGEST_FIRST give identical results.  EQUAL_SHARES (groups of
+ * more than 16 heads, at most 2048 sequences): as many workgroups as the
+ * device holds at once each walk an equal share of the batch's cache tiles,
+ * across sequence boundaries, and the pieces of a sequence are merged after;
+ * its results differ from the partitioned schedules only by rounding. */
 typedef enum {
-  PA_SCHEDULE_AUTO = 0,          /* longest first for groups of more than 16 heads */
+  PA_SCHEDULE_AUTO = 0,          /* groups of more than 16 heads, when the plan
+                                    splits: equal shares if the batch has fewer
+                                    (kv head, sequence) items than the CUs hold
+                                    decode workgroups, else longest first; other
+                                    groups: the grid's order                      */
   PA_SCHEDULE_GRID = 1,          /* the grid's order (partition-major)              */
-  PA_SCHEDULE_LONGEST_FIRST = 2  /* longest first whenever the plan splits (MFMA)   */
+  PA_SCHEDULE_LONGEST_FIRST = 2, /* longest first whenever the plan splits (MFMA)   */
+  PA_SCHEDULE_EQUAL_SHARES = 3   /* equal shares where they apply (see above), even
+                                    when the auto plan would not split; otherwise
+                                    as AUTO without equal shares                   */
 } pa_schedule;
 
 /* Optional overrides (pass NULL for the defaults). */
@@ -149,10 +161,14 @@ typedef struct {
 
 /* A launch plan (output of paged_attention_plan). */
 typedef struct {
-  int32_t num_partitions; /* partitions per sequence; 1 = single pass, no reduce  */
-  int32_t partition_size; /* tokens per partition (multiple of block_size)         */
+  int32_t num_partitions; /* partitions per sequence; 1 = single pass, no reduce.
+                             EQUAL_SHARES: the most workgroups the call launches
+                             (CUs times what the kernel's LDS lets one CU hold)  */
+  int32_t partition_size; /* tokens per partition (multiple of block_size);
+                             0 for EQUAL_SHARES                                   */
   int32_t engine;         /* resolved pa_engine                                     */
-  int32_t schedule;       /* resolved: PA_SCHEDULE_GRID or PA_SCHEDULE_LONGEST_FIRST */
+  int32_t schedule;       /* resolved: PA_SCHEDULE_GRID, _LONGEST_FIRST or
+                             _EQUAL_SHARES                                          */
   size_t workspace_bytes; /* workspace this plan uses (0 for a single pass)         */
 } pa_plan;
 
@@ -182,6 +198,9 @@ typedef struct {
  *
  * With opts == NULL an undersized workspace makes the planner use fewer
  * partitions (down to a single pass); it never fails for lack of workspace.
+ * An equal-share plan (pa_schedule) launches the CUs' count times as many
+ * workgroups of the decode kernel as one CU holds on the current device; the
+ * call looks that occupancy up once per device and configuration.
  */
 int paged_attention_decode(void* out, const void* query, const void* key_cache,
                            const void* value_cache, const int32_t* block_tables,

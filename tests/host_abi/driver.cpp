@@ -103,13 +103,14 @@ static void split_small_batch() {
 static void mqa_longest_first() {
   g_launches.clear();
   pa_dims d = dims(256, 48, 1, 128, 16, 70000, 512, PA_F16);
-  const size_t ws = paged_attention_workspace_bytes(&d, nullptr);
+  const pa_opts o = {0, PA_ENGINE_AUTO, 0, PA_SCHEDULE_LONGEST_FIRST};
+  const size_t ws = paged_attention_workspace_bytes(&d, &o);
   char* w = FAKE + (1 << 20);
   const float slopes = 0.f;
   CHECK(paged_attention_decode(FAKE, FAKE, FAKE, FAKE + (1 << 28), reinterpret_cast<const int32_t*>(FAKE),
                                reinterpret_cast<const int32_t*>(FAKE), 0.088f, 16,
                                reinterpret_cast<const float*>(FAKE + 64), nullptr, &d, w, ws,
-                               nullptr) == PA_OK);
+                               &o) == PA_OK);
   (void)slopes;
   CHECK(g_launches.size() == 3);
   CHECK(std::strcmp(g_launches[0].kind, "order") == 0);
@@ -121,6 +122,35 @@ static void mqa_longest_first() {
   const char* order = reinterpret_cast<const char*>(a.unit_order);
   CHECK(order >= w && order + 256 * 2 * 4 <= w + ws);
   CHECK(a.alibi == reinterpret_cast<const float*>(FAKE + 64));
+}
+
+static void mqa_equal_shares() {
+  g_launches.clear();
+  pa_dims d = dims(64, 48, 1, 128, 16, 70000, 512, PA_F16);  // fewer items than CUs: equal shares
+  const size_t ws = paged_attention_workspace_bytes(&d, nullptr);
+  char* w = FAKE + (1 << 20);
+  CHECK(paged_attention_decode(FAKE, FAKE, FAKE, FAKE + (1 << 28), reinterpret_cast<const int32_t*>(FAKE),
+                               reinterpret_cast<const int32_t*>(FAKE), 0.088f, 16, nullptr, nullptr, &d, w,
+                               ws, nullptr) == PA_OK);
+  CHECK(g_launches.size() == 2);
+  CHECK(std::strcmp(g_launches[0].kind, "mfma") == 0);
+  CHECK(std::strcmp(g_launches[1].kind, "reduce") == 0);
+  const pa::DecodeArgs& a = g_launches[0].a;
+  // one workgroup per CU; slots for 64 items and 256 workgroups
+  CHECK(a.stream_wgs == kStubCus && a.num_slots == 64 + kStubCus && a.unit_order == nullptr);
+  CHECK(a.piece_cost == 24);
+  CHECK(g_launches[1].a.stream_wgs == a.stream_wgs && g_launches[1].a.ws_pfx == a.ws_pfx);
+  const char* o = reinterpret_cast<const char*>(a.ws_o);
+  const char* ml = reinterpret_cast<const char*>(a.ws_ml);
+  const char* pfx = reinterpret_cast<const char*>(a.ws_pfx);
+  CHECK(o == w && ml >= o + (size_t)a.num_slots * 48 * 128 * 4 && pfx >= ml + (size_t)a.num_slots * 48 * 8);
+  CHECK(pfx + 65 * 4 <= w + ws);
+  // too little workspace for the shares: a partitioned plan that fits
+  g_launches.clear();
+  CHECK(paged_attention_decode(FAKE, FAKE, FAKE, FAKE + (1 << 28), reinterpret_cast<const int32_t*>(FAKE),
+                               reinterpret_cast<const int32_t*>(FAKE), 0.088f, 16, nullptr, nullptr, &d, w,
+                               ws - 1, nullptr) == PA_OK);
+  for (const Launch& l : g_launches) CHECK(l.a.stream_wgs == 0);
 }
 
 static void fp8_cache() {
@@ -276,6 +306,7 @@ int main() {
   joint_layout();
   split_small_batch();
   mqa_longest_first();
+  mqa_equal_shares();
   fp8_cache();
   mha_valu_and_forced_engines();
   prefill();

@@ -53,6 +53,10 @@ hipError_t launch_partition_reduce(const DecodeArgs& a, int dtype, int head_size
   record("reduce", &a, dtype, head_size, false);
   return hipSuccess;
 }
+hipError_t staged_decode_occupancy(int, int head_size, int group, bool kv_fp8, int* wgs) {
+  *wgs = staged_decode_wgs_per_cu(head_size, group, kv_fp8);
+  return hipSuccess;
+}
 hipError_t launch_unit_order(const DecodeArgs& a, int32_t* order, hipStream_t) {
   record("order", &a, 0, 0, false);
   g_launches.back().ptr = order;

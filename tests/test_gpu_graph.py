@@ -21,9 +21,13 @@ DECODE_CASES = {
     # small batch, long context: split partitions + reduce
     "gqa_split": dict(num_seqs=2, num_heads=64, num_kv_heads=8, head_size=128, block_size=16,
                       dtype="bf16", context_lens=3000),
-    # 48-head groups, ragged, ALiBi: unit-order kernel + staged decode + reduce
+    # 48-head groups, ragged, ALiBi: equal shares of the staged decode + reduce
+    "mqa_equal_shares": dict(num_seqs=32, num_heads=48, num_kv_heads=1, head_size=128,
+                             block_size=16, dtype="f16", context_lens=(64, 4000), alibi=True),
+    # the same cut into partitions: unit-order kernel + staged decode + reduce
     "mqa_longest_first": dict(num_seqs=32, num_heads=48, num_kv_heads=1, head_size=128,
-                              block_size=16, dtype="f16", context_lens=(64, 4000), alibi=True),
+                              block_size=16, dtype="f16", context_lens=(64, 4000), alibi=True,
+                              schedule="longest_first"),
     # FP8 cache, one pass
     "gqa_fp8_single": dict(num_seqs=64, num_heads=64, num_kv_heads=8, head_size=128,
                            block_size=16, dtype="bf16", context_lens=700, kv_dtype="fp8"),
@@ -63,12 +67,15 @@ def capture_and_check(call, query, what):
 @pytest.mark.parametrize("case", list(DECODE_CASES))
 def test_decode_graph_replay(case):
     dev = device()
-    inp = to_device(make(seed=31, poison=True, **DECODE_CASES[case]), dev)
+    args = dict(DECODE_CASES[case])
+    schedule = args.pop("schedule", "auto")
+    inp = to_device(make(seed=31, poison=True, **args), dev)
 
     def call(out, ws):
         paged_attention_decode(out, inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
                                inp.context_lens, inp.scale, inp.block_size, inp.alibi_slopes,
-                               workspace=ws, k_scale=inp.k_scale, v_scale=inp.v_scale)
+                               workspace=ws, k_scale=inp.k_scale, v_scale=inp.v_scale,
+                               schedule=schedule)
 
     capture_and_check(call, inp.query, case)
 

@@ -11,7 +11,7 @@ partitions where the auto plan is a single pass):
     256, joint cache layout (16 sequences sampled);
   * the same with an FP8 E4M3 cache;
   * MQA 48/1 fp16 ragged 64..8192 with ALiBi, batch 256 (the LDS-staged path
-    of groups above 16 heads, split, longest first);
+    of groups above 16 heads: equal shares, and split partitions);
   * 8-token blocks with contexts past the 512-tile LDS window of tile
     source offsets that the staged path keeps (refills at 4096, 8192 ...
     tokens),
@@ -29,14 +29,15 @@ from workloads import workload_args
 pytestmark = pytest.mark.gpu
 
 
-def plan_of(inp, engine="auto", partition_size=0):
+def plan_of(inp, engine="auto", partition_size=0, schedule="auto"):
     dims = make_dims(inp.query, inp.key_cache, inp.block_tables, inp.k_scale, inp.v_scale,
                      kv_layout_of(inp.key_cache, inp.value_cache))
-    return paged_attention_plan(dims, 1 << 40, make_opts(partition_size, engine))
+    return paged_attention_plan(dims, 1 << 40, make_opts(partition_size, engine, schedule=schedule))
 
 
 def check_needles(inp, seqs, runs, boundaries, what):
-    """Plant needles in `seqs`, then compare every (engine, partition size) run."""
+    """Plant needles in `seqs`, then compare every (engine, partition size[,
+    schedule]) run."""
     lens = inp.context_lens.cpu().numpy()
     Hq = inp.query.shape[1]
     pos = {s: needles.positions_for(int(lens[s]), Hq, inp.block_size, boundaries, seed=s)
@@ -45,12 +46,13 @@ def check_needles(inp, seqs, runs, boundaries, what):
     ref = oracle_ref(inp, seqs)
     for i, s in enumerate(seqs):   # the needles hold: the exact output is the value row
         assert np.abs(ref[i] - planted["v"][s]).max() <= 1e-6 * max(1.0, np.abs(ref[i]).max())
-    for engine, ps in runs:
-        p = plan_of(inp, engine, ps)
-        out = run(inp, engine=engine, partition_size=ps)
+    for r in runs:
+        engine, ps, schedule = r if len(r) == 3 else r + ("auto",)
+        p = plan_of(inp, engine, ps, schedule)
+        out = run(inp, engine=engine, partition_size=ps, schedule=schedule)
         compare(out, ref, inp.dtype, seqs,
-                what=f"{what} engine={engine} partition={ps} (plan: {p.num_partitions} x "
-                     f"{p.partition_size})")
+                what=f"{what} engine={engine} partition={ps} schedule={schedule} (plan: "
+                     f"{p.num_partitions} x {p.partition_size}, schedule {p.schedule})")
 
 
 @pytest.mark.parametrize("kv", ["native", "fp8"])
@@ -73,10 +75,13 @@ def test_mqa_ragged_alibi_needles(kv):
     lens = inp.context_lens.cpu().numpy()
     # the sample: the longest and shortest sequences plus seeded ones
     seqs = sorted(set(sample_seqs(256, 14, seed=12)) | {int(np.argmax(lens)), int(np.argmin(lens))})
-    auto = plan_of(inp)
-    assert auto.num_partitions > 1, "the MQA batch is expected to split"
-    bounds = tuple(auto.partition_size * k for k in range(1, auto.num_partitions)) + (1024, 2048)
-    runs = [("auto", 0), ("mfma", -1), ("mfma", 1024), ("valu", 0)]
+    parts = plan_of(inp, schedule="longest_first")
+    assert parts.num_partitions > 1, "the MQA batch is expected to split"
+    bounds = tuple(parts.partition_size * k for k in range(1, parts.num_partitions)) + (1024, 2048)
+    # auto (partitions, longest first), in grid order; equal shares (needles at
+    # their own cuts: tests/test_gpu_shares.py); one pass; the VALU engine
+    runs = [("auto", 0), ("mfma", 0, "grid"), ("mfma", 0, "equal_shares"), ("mfma", -1),
+            ("mfma", 1024), ("valu", 0)]
     check_needles(inp, seqs, runs, boundaries=bounds, what=f"mqa ragged alibi {kv}")
     # the grid order of the same split gives the same bits
     a = run(inp, engine="mfma", schedule="grid")

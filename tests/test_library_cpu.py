@@ -286,8 +286,8 @@ def test_plan_one_tile_targets_one_group_per_cu(L):
                        (16, 64, 2), (64, 256, 1)):
         st, p = plan(L, dims(S=S, MAXB=maxb))
         assert st == OK and p.engine == 2 and p.num_partitions == P, (S, maxb, p.num_partitions)
-    # a 48-head group (three tiles) keeps two workgroups per CU
-    st, p = plan(L, dims(S=64, Hq=48, Hkv=1, MAXB=256))
+    # a 48-head group (three tiles) cut into partitions keeps two workgroups per CU
+    st, p = plan(L, dims(S=64, Hq=48, Hkv=1, MAXB=256), schedule=2)
     assert st == OK and p.num_partitions == 8
     # over an FP8 cache: two per CU, partitions of 128+ tokens
     for S, maxb, P in ((1, 256, 32), (4, 256, 16), (16, 256, 4), (1, 64, 8), (4, 64, 8),
@@ -300,14 +300,59 @@ def test_plan_one_tile_targets_one_group_per_cu(L):
 
 def test_plan_multi_tile_partitions(L):
     # 48-head MQA, batch 256, contexts up to 8192: two partitions per sequence
-    st, p = plan(L, dims(S=256, Hq=48, Hkv=1, MAXB=512))
-    assert st == OK and p.engine == 2 and p.num_partitions == 2
+    # when the work is cut into partitions
+    st, p = plan(L, dims(S=256, Hq=48, Hkv=1, MAXB=512), schedule=2)
+    assert st == OK and p.engine == 2 and p.num_partitions == 2 and p.partition_size == 4096
+
+
+def test_plan_equal_shares(L):
+    GRID, LONGEST, SHARES = 1, 2, 3
+    mqa = dims(S=64, Hq=48, Hkv=1, MAXB=512)
+    # auto, fewer items than workgroup slots: equal shares, one 12-wave workgroup
+    # per CU (its LDS ring holds one)
+    st, p = plan(L, mqa)
+    assert st == OK and p.schedule == SHARES and p.engine == 2
+    assert p.num_partitions == 256 and p.partition_size == 0
+    # workspace: fp32 partials of 48 heads x (64 items + 256 workgroups) slots, (m, l)
+    # pairs, the tile prefix
+    slots, rows = 64 + 256, 48
+    assert p.workspace_bytes >= slots * rows * (128 * 4 + 8) + 65 * 4
+    # as many items as workgroup slots: longest-first partitions; on request, shares
+    st, q = plan(L, dims(S=256, Hq=48, Hkv=1, MAXB=512))
+    assert st == OK and q.schedule == LONGEST and q.num_partitions == 2
+    st, q = plan(L, dims(S=256, Hq=48, Hkv=1, MAXB=512), schedule=SHARES)
+    assert st == OK and q.schedule == SHARES and q.num_partitions == 256
+    o = PaOpts(0, 0, 256, 0)
+    assert L.paged_attention_workspace_bytes(ctypes.byref(mqa), ctypes.byref(o)) == p.workspace_bytes
+    # a workspace too small for the shares falls back to partitions that fit
+    st, q = plan(L, mqa, ws=p.workspace_bytes - 1)
+    assert st == OK and q.schedule != SHARES and q.workspace_bytes < p.workspace_bytes
+    # 32-head groups (4-wave workgroups, two per CU by LDS), 64-head groups (four):
+    # 256 items are fewer than their workgroup slots
+    st, p = plan(L, dims(S=256, Hq=32, Hkv=1, MAXB=512))
+    assert st == OK and p.schedule == SHARES and p.num_partitions == 2 * 256
+    st, p = plan(L, dims(S=256, Hq=64, Hkv=1, MAXB=512))
+    assert st == OK and p.schedule == SHARES and p.num_partitions == 4 * 256
+    # requested: even where the auto plan makes one pass
+    st, p = plan(L, dims(S=1024, Hq=48, Hkv=1, MAXB=64))
+    assert st == OK and p.schedule == GRID and p.num_partitions == 1
+    st, p = plan(L, dims(S=1024, Hq=48, Hkv=1, MAXB=64), schedule=SHARES)
+    assert st == OK and p.schedule == SHARES and p.num_partitions == 256
+    # not for one head tile, nor for more than 2048 sequences, nor with a forced partition size
+    st, p = plan(L, dims(S=4), schedule=SHARES)
+    assert st == OK and p.schedule == GRID
+    st, p = plan(L, dims(S=2048, Hq=48, Hkv=1, MAXB=4), schedule=SHARES)
+    assert st == OK and p.schedule == SHARES
+    st, p = plan(L, dims(S=2049, Hq=48, Hkv=1, MAXB=4), schedule=SHARES)
+    assert st == OK and p.schedule != SHARES
+    st, p = plan(L, mqa, ps=1024, schedule=SHARES)
+    assert st == OK and p.schedule == LONGEST and p.partition_size == 1024
 
 
 def test_plan_schedule(L):
     GRID, LONGEST = 1, 2
     mqa = dims(S=256, Hq=48, Hkv=1, MAXB=512)
-    st, p = plan(L, mqa)                                   # split, > 16 heads: longest first
+    st, p = plan(L, mqa, schedule=LONGEST)                 # split, > 16 heads: longest first
     assert st == OK and p.num_partitions > 1 and p.schedule == LONGEST
     st, g = plan(L, mqa, schedule=GRID)
     assert st == OK and g.schedule == GRID and g.num_partitions == p.num_partitions
@@ -321,12 +366,12 @@ def test_plan_schedule(L):
     assert st == OK and p.num_partitions == 1 and p.schedule == GRID and p.workspace_bytes == 0
     st, p = plan(L, dims(S=4, Hq=8, Hkv=8), schedule=LONGEST)  # VALU engine keeps the grid
     assert st == OK and p.engine == 1 and p.schedule == GRID
-    assert plan(L, dims(), schedule=3)[0] == INVALID
+    assert plan(L, dims(), schedule=4)[0] == INVALID
     assert plan(L, dims(), schedule=-1)[0] == INVALID
     d = dims(S=256, Hq=48, Hkv=1, MAXB=512)
-    o = PaOpts(0, 0, 256, 0)
+    o = PaOpts(0, 0, 256, LONGEST)
     assert L.paged_attention_workspace_bytes(ctypes.byref(d), ctypes.byref(o)) == \
-        plan(L, d)[1].workspace_bytes
+        plan(L, d, schedule=LONGEST)[1].workspace_bytes
 
 
 def test_status_strings(L):
