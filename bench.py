@@ -48,8 +48,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-size", type=int, default=0)
-    ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "longest_first"],
-                    help="order of the work units of a split plan (see pa_schedule)")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "longest_first", "equal_shares"],
+                    help="layout of a split plan's work over workgroups (see pa_schedule)")
     ap.add_argument("--kv-dtype", default=None, choices=["fp8"],
                     help="store the K/V caches as FP8 E4M3 (scale 1/16) instead of the query type")
     ap.add_argument("--kv-layout", default="joint", choices=["joint", "separate"],
@@ -543,7 +543,7 @@ def measure_decode(args, *, steps, warmup, engine="auto", partition_size=0, sche
 def plan_fields(plan, engine="auto"):
     return {"engine": {0: "auto", 1: "valu", 2: "mfma"}[plan.engine] if engine == "auto" else engine,
             "num_partitions": plan.num_partitions, "partition_size": plan.partition_size,
-            "schedule": {2: "longest_first"}.get(plan.schedule, "grid")}
+            "schedule": {2: "longest_first", 3: "equal_shares"}.get(plan.schedule, "grid")}
 
 
 def grid_rows(steps, warmup, kv_layout, headline=None):

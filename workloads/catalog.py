@@ -30,10 +30,10 @@ WORKLOADS = {
                         dtype="bf16", context_lens=4096, alibi=False, seed_base=3000,
                         batches=(1, 4, 16, 64, 256)),
     # MQA, 48 query heads / 1 KV head, ragged lengths 64..8192, ALiBi slopes
-    # 2^(-8 i / 48), fp16, batch 256.
+    # 2^(-8 i / 48), fp16, batch 256 (and 32: fewer sequences than CUs).
     "mqa_ragged_alibi": dict(num_seqs=256, num_heads=48, num_kv_heads=1, head_size=128,
                              block_size=16, dtype="f16", context_lens=(64, 8192),
-                             alibi=True, seed_base=4000, batches=(256,)),
+                             alibi=True, seed_base=4000, batches=(32, 256)),
 }
 
 # The headline measurement: GQA 64/8 bf16, context 4096, batch 256.
