@@ -51,6 +51,35 @@ def test_random_decode(seed):
     compare(out, ref, c["dtype"], what=f"seed {seed}: {c}")
 
 
+@pytest.mark.parametrize("seed", range(32))
+def test_random_decode_equal_shares(seed):
+    """Random staged configurations (groups of 17..64 heads) in equal shares:
+    batches from one sequence to 40, lengths from 0, several kv heads."""
+    dev = device()
+    rng = np.random.default_rng(3000 + seed)
+    G = int(rng.choice([20, 24, 32, 40, 48, 64]))
+    Hkv = int(rng.integers(1, 4))
+    D = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    BS = int(rng.choice(BLOCKS))
+    S = int(rng.integers(1, 41))
+    hi = int(rng.choice([30, 600, 3000]))
+    lens = [int(x) for x in rng.integers(0, hi, size=S)]
+    fp8 = bool(rng.integers(0, 3) == 0)
+    alibi = bool(rng.integers(0, 2))
+    layout = str(rng.choice(["separate", "joint"]))
+    inp = to_device(make(num_seqs=S, num_heads=G * Hkv, num_kv_heads=Hkv, head_size=D, block_size=BS,
+                         dtype=dtype, seed=seed, context_lens=lens, alibi=alibi, poison=True,
+                         kv_dtype="fp8" if fp8 else None, kv_layout=layout), dev)
+    seqs = list(range(S)) if S <= 12 else sorted(set(rng.choice(S, 12, replace=False).tolist()))
+    ref = oracle_ref(inp, seqs)
+    out = run(inp, schedule="equal_shares")
+    what = f"seed {seed}: G={G} Hkv={Hkv} D={D} {dtype} BS={BS} S={S} fp8={fp8} alibi={alibi} {layout}"
+    compare(out, ref, dtype, seqs, what=what)
+    lens_np = np.asarray(lens)
+    assert (out[torch.as_tensor(np.flatnonzero(lens_np == 0), device=out.device, dtype=torch.long)] == 0).all(), what
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_random_prefill(seed):
     dev = device()
