@@ -6,8 +6,10 @@
 //
 // Decomposition.  A workgroup owns the query heads that share one kv head (the
 // GQA group, padded to NT tiles of 16 heads), for one sequence and one context
-// partition.  A head tile is the N = 16 side of the MFMA products and each
-// 16-row tile of cached tokens is the M = 16 side:
+// partition -- or, under the equal-share schedule of the staged kernel (STREAM),
+// for the pieces of (kv head, sequence) items that its equal share of the
+// batch's tiles meets, one after the other.  A head tile is the N = 16 side of
+// the MFMA products and each 16-row tile of cached tokens is the M = 16 side:
 //
 //   S^T[t, g]   = sum_d K[t, d] q[g, d]    v_mfma_f32_16x16x32_{f16,bf16}, D/32 steps
 //   O^T[d, g]  += sum_t V[t, d] P[g, t]     v_mfma_f32_16x16x16_{f16,bf16}, D/16 tiles

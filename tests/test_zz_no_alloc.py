@@ -25,7 +25,8 @@ def both(inp, **kw):
     dims = make_dims(inp.query, inp.key_cache, inp.block_tables, inp.k_scale, inp.v_scale,
                      kv_layout_of(inp.key_cache, inp.value_cache))
     plan = paged_attention_plan(dims, NOALLOC_SCRATCH_BYTES,
-                                make_opts(kw.get("partition_size", 0), kw.get("engine", "auto")))
+                                make_opts(kw.get("partition_size", 0), kw.get("engine", "auto"),
+                                          schedule=kw.get("schedule", "auto")))
     return a, b, plan
 
 
@@ -35,11 +36,16 @@ CASES = [
                        dtype="bf16", context_lens=4096),
      dict(num_seqs=1, num_heads=64, num_kv_heads=8, head_size=128, block_size=16, dtype="bf16",
           context_lens=1500), {}),
-    ("mqa ragged alibi, longest first",
+    ("mqa ragged alibi, equal shares",
      dict(num_seqs=96, num_heads=48, num_kv_heads=1, head_size=128, block_size=16, dtype="f16",
           context_lens=(64, 8192), alibi=True),
      dict(num_seqs=20, num_heads=48, num_kv_heads=1, head_size=128, block_size=16, dtype="f16",
           context_lens=(64, 3000), alibi=True), {}),
+    ("mqa ragged alibi, longest first",
+     dict(num_seqs=96, num_heads=48, num_kv_heads=1, head_size=128, block_size=16, dtype="f16",
+          context_lens=(64, 8192), alibi=True),
+     dict(num_seqs=20, num_heads=48, num_kv_heads=1, head_size=128, block_size=16, dtype="f16",
+          context_lens=(64, 3000), alibi=True), dict(schedule="longest_first")),
     ("fp8 cache, forced partitions",
      dict(num_seqs=8, num_heads=16, num_kv_heads=2, head_size=128, block_size=16, dtype="bf16",
           context_lens=(1, 3000), kv_dtype="fp8", alibi=True),
