@@ -37,7 +37,10 @@ DECODE_CASES = {
 }
 
 
-def capture_and_check(call, query, what):
+def capture_and_check(call, query, what, lens=None, max_len=0):
+    """Capture `call` into a graph and replay it four times, writing new query
+    values (and, with `lens`, new context lengths up to `max_len`) between
+    replays as a decode loop would; every replay must equal an eager call."""
     dev = query.device
     ws_g = torch.empty(WS_BYTES, dtype=torch.uint8, device=dev)
     ws_e = torch.empty(WS_BYTES, dtype=torch.uint8, device=dev)
@@ -54,6 +57,9 @@ def capture_and_check(call, query, what):
     gen = torch.Generator(device=dev).manual_seed(11)
     for rep in range(4):
         query.copy_(torch.randn(query.shape, generator=gen, device=dev).to(query.dtype))
+        if lens is not None:  # the batch's lengths move between steps (within the plan's bound)
+            lens.copy_(torch.randint(0, max_len + 1, lens.shape, generator=gen, device=dev,
+                                     dtype=lens.dtype))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -78,6 +84,26 @@ def test_decode_graph_replay(case):
                                schedule=schedule)
 
     capture_and_check(call, inp.query, case)
+
+
+@pytest.mark.parametrize("schedule", ["equal_shares", "longest_first"])
+def test_decode_graph_replay_with_moving_lengths(schedule):
+    """The split plan is fixed at capture (it depends only on the host-known
+    bound max_blocks_per_seq * block_size); the device-side schedule -- the
+    equal shares' tile prefix, the longest-first order -- is rebuilt from the
+    lengths on every replay."""
+    dev = device()
+    inp = to_device(make(seed=33, num_seqs=24, num_heads=48, num_kv_heads=1, head_size=128,
+                         block_size=16, dtype="f16", context_lens=(64, 4000), alibi=True), dev)
+    max_len = inp.block_tables.shape[1] * inp.block_size
+
+    def call(out, ws):
+        paged_attention_decode(out, inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
+                               inp.context_lens, inp.scale, inp.block_size, inp.alibi_slopes,
+                               workspace=ws, schedule=schedule)
+
+    capture_and_check(call, inp.query, f"moving lengths, {schedule}", lens=inp.context_lens,
+                      max_len=max_len)
 
 
 def test_prefill_graph_replay():
