@@ -203,9 +203,10 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
   // Grid schedules: one unit (row chunk, kv head, sequence, partition) per
   // workgroup.  Equal shares (decode on the staged kernel, stream_wgs > 0):
   // the batch's tiles, walked item by item (item = kv head * num_seqs +
-  // sequence), are cut into gridDim.x consecutive shares of equal length, and
-  // the workgroup processes the pieces of the items its share meets, one after
-  // the other (pieces of one item from several workgroups meet in the reduce).
+  // sequence), are cut into consecutive shares of equal cost (tiles plus a
+  // fixed cost per item; below), one per workgroup, and the workgroup
+  // processes the pieces of the items its share meets, one after the other
+  // (pieces of one item from several workgroups meet in the reduce).
   // A unit (piece): rows of row chunk / kv head xi of sequence seq, tiles
   // t_lo .. t_hi - 1 of the sequence (tiles of TT tokens).
   constexpr bool stream = STREAM;

@@ -375,7 +375,7 @@ def test_longest_first_schedule(group, Hkv):
 
 # ---------------------------------------------------------------------------
 # The reduce at every partition count it handles differently: batches of 4,
-# 8 and 16 partial-output loads, and more than 64 partitions (the (m, l)
+# 8, 16 and 32 partial-output loads, and more than 64 partitions (the (m, l)
 # pairs then take several passes of one partition per lane).
 # ---------------------------------------------------------------------------
 
