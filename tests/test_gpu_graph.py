@@ -106,6 +106,33 @@ def test_decode_graph_replay_with_moving_lengths(schedule):
                       max_len=max_len)
 
 
+def test_equal_shares_first_call_under_capture():
+    """The first equal-share call of a configuration looks up the decode
+    kernel's occupancy on the device; made under graph capture (a configuration
+    -- bf16, head size 64, 33..48-head groups, FP8 cache -- that the tests
+    before this one do not run), it must still capture and replay correctly."""
+    dev = device()
+    inp = to_device(make(seed=34, num_seqs=20, num_heads=40, num_kv_heads=1, head_size=64,
+                         block_size=16, dtype="bf16", context_lens=(1, 3000), alibi=True,
+                         kv_dtype="fp8"), dev)
+    ws_g = torch.empty(WS_BYTES, dtype=torch.uint8, device=dev)
+    out_g = torch.full_like(inp.query, float("nan"))
+    args = (inp.query, inp.key_cache, inp.value_cache, inp.block_tables, inp.context_lens, inp.scale,
+            inp.block_size, inp.alibi_slopes)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        paged_attention_decode(out_g, *args, workspace=ws_g, k_scale=inp.k_scale, v_scale=inp.v_scale,
+                               schedule="equal_shares")
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        out_e = torch.full_like(inp.query, float("nan"))
+        paged_attention_decode(out_e, *args, workspace=torch.empty_like(ws_g), k_scale=inp.k_scale,
+                               v_scale=inp.v_scale, schedule="equal_shares")
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {rep} differs from the eager call"
+
+
 def test_prefill_graph_replay():
     dev = device()
     inp, q, qs, max_q = prefill_inputs(new_tokens=[40, 1, 300, 7], seed=32, device=dev,
