@@ -141,6 +141,43 @@ def _owned_workspace(nbytes: int, device, stream):
     return ws
 
 
+# The (dims, opts) structures of recent decode calls, by everything they hold:
+# a serving loop repeats one configuration every step, and building the ctypes
+# structures costs more than the lookup.  The library only reads them.
+_decode_struct_cache: dict = {}
+
+
+def _decode_structs(out, query, key_cache, value_cache, block_tables, context_lens, alibi_slopes,
+                    k_scale, v_scale, partition_size, engine, schedule):
+    """Checks every tensor of a decode call; returns its (dims, opts)."""
+    _check_attention_shapes(out, query, key_cache, value_cache, block_tables, context_lens,
+                            alibi_slopes, query.shape[0] if query.dim() == 3 else 0)
+    qdt = query.dtype
+    _require(out, "out", qdt)
+    _require(query, "query", qdt)
+    kdt = key_cache.dtype
+    kv_dtype = kdt if kdt == torch.float8_e4m3fn else qdt
+    _require(key_cache, "key_cache", kv_dtype, dense=False)
+    _require(value_cache, "value_cache", kv_dtype, dense=False)
+    layout = kv_layout_of(key_cache, value_cache)
+    _require(block_tables, "block_tables", torch.int32)
+    _require(context_lens, "context_lens", torch.int32)
+    if alibi_slopes is not None:
+        _require(alibi_slopes, "alibi_slopes", torch.float32)
+    if qdt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {qdt}")
+    key = (query.shape, key_cache.shape, block_tables.shape[1], qdt, kdt, k_scale, v_scale, layout,
+           partition_size, engine, schedule)
+    structs = _decode_struct_cache.get(key)
+    if structs is None:
+        structs = (make_dims(query, key_cache, block_tables, k_scale, v_scale, layout),
+                   make_opts(partition_size, engine, schedule=schedule))
+        if len(_decode_struct_cache) >= 64:
+            _decode_struct_cache.clear()
+        _decode_struct_cache[key] = structs
+    return structs
+
+
 def paged_attention_plan(dims: PaDims, workspace_bytes: int, opts: Optional[PaOpts] = None) -> PaPlan:
     plan = PaPlan()
     check(lib().paged_attention_plan(ctypes.byref(dims), workspace_bytes,
@@ -166,22 +203,8 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
     code * k_scale / code * v_scale.  ``workspace`` (uint8 device tensor) is
     allocated with torch when omitted and the plan needs one.
     """
-    _check_attention_shapes(out, query, key_cache, value_cache, block_tables, context_lens,
-                            alibi_slopes, query.shape[0] if query.dim() == 3 else 0)
-    _require(out, "out", query.dtype)
-    _require(query, "query", query.dtype)
-    kv_dtype = torch.float8_e4m3fn if key_cache.dtype == torch.float8_e4m3fn else query.dtype
-    _require(key_cache, "key_cache", kv_dtype, dense=False)
-    _require(value_cache, "value_cache", kv_dtype, dense=False)
-    layout = kv_layout_of(key_cache, value_cache)
-    _require(block_tables, "block_tables", torch.int32)
-    _require(context_lens, "context_lens", torch.int32)
-    if alibi_slopes is not None:
-        _require(alibi_slopes, "alibi_slopes", torch.float32)
-    if query.dtype not in _DTYPE:
-        raise ValueError(f"unsupported dtype {query.dtype}")
-    dims = make_dims(query, key_cache, block_tables, k_scale, v_scale, layout)
-    opts = make_opts(partition_size, engine, schedule=schedule)
+    dims, opts = _decode_structs(out, query, key_cache, value_cache, block_tables, context_lens,
+                                 alibi_slopes, k_scale, v_scale, partition_size, engine, schedule)
     if workspace is None:
         nbytes = paged_attention_workspace_bytes(dims, opts)
         if nbytes:
@@ -208,22 +231,8 @@ def paged_attention_decode_noalloc(out: torch.Tensor, query: torch.Tensor, key_c
     """paged_attention_decode without a workspace: the split partials go to the
     library's per-GPU scratch (see paged_attention_decode_noalloc in the C
     header; calls that overlap on one GPU race).  Allocates nothing."""
-    _check_attention_shapes(out, query, key_cache, value_cache, block_tables, context_lens,
-                            alibi_slopes, query.shape[0] if query.dim() == 3 else 0)
-    _require(out, "out", query.dtype)
-    _require(query, "query", query.dtype)
-    kv_dtype = torch.float8_e4m3fn if key_cache.dtype == torch.float8_e4m3fn else query.dtype
-    _require(key_cache, "key_cache", kv_dtype, dense=False)
-    _require(value_cache, "value_cache", kv_dtype, dense=False)
-    layout = kv_layout_of(key_cache, value_cache)
-    _require(block_tables, "block_tables", torch.int32)
-    _require(context_lens, "context_lens", torch.int32)
-    if alibi_slopes is not None:
-        _require(alibi_slopes, "alibi_slopes", torch.float32)
-    if query.dtype not in _DTYPE:
-        raise ValueError(f"unsupported dtype {query.dtype}")
-    dims = make_dims(query, key_cache, block_tables, k_scale, v_scale, layout)
-    opts = make_opts(partition_size, engine, schedule=schedule)
+    dims, opts = _decode_structs(out, query, key_cache, value_cache, block_tables, context_lens,
+                                 alibi_slopes, k_scale, v_scale, partition_size, engine, schedule)
     check(lib().paged_attention_decode_noalloc(
         out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         block_tables.data_ptr(), context_lens.data_ptr(), float(scale), int(block_size),
