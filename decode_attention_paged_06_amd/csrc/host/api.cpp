@@ -602,8 +602,10 @@ static int check_copy_args(int32_t num_tokens, int32_t num_kv_heads, int32_t hea
   const long long row_bytes = (long long)head_size * elem_bytes(dtype);
   if (head_size <= 0 || row_bytes % 16 != 0)
     return fail(PA_ERR_UNSUPPORTED, "head_size %d (a row must be a multiple of 16 bytes)", head_size);
-  if ((unsigned long long)num_tokens * num_kv_heads * (row_bytes / 16) >= (1ULL << 32))
-    return fail(PA_ERR_INVALID_ARG, "num_tokens * num_kv_heads * head_size too large");
+  // the kernels index 16-byte pieces with 32-bit counters that step by up to
+  // 2^24 (their grid): below 2^31 pieces no step can wrap around
+  if ((unsigned long long)num_tokens * num_kv_heads * (row_bytes / 16) >= (1ULL << 31))
+    return fail(PA_ERR_INVALID_ARG, "num_tokens * num_kv_heads * head_size too large (2^31 16-byte pieces or more)");
   if ((unsigned long long)num_blocks * block_size > 0x7fffffffULL)
     return fail(PA_ERR_INVALID_ARG, "num_blocks * block_size exceeds the int32 slot range");
   return PA_OK;

@@ -307,7 +307,9 @@ int paged_attention_prefill_plan(const pa_dims* dims, int32_t num_query_tokens,
  *                     < num_blocks * block_size (device-side precondition).
  * dtype: PA_F16, PA_BF16 or PA_FP8_E4M3 (bytes are moved, never converted).
  * A row (head_size elements) must be a multiple of 16 bytes; data pointers
- * 16-byte aligned.  Any block_size >= 1 is accepted.
+ * 16-byte aligned.  Any block_size >= 1 is accepted.  The rows moved
+ * (num_tokens * num_kv_heads * head_size elements) must be fewer than 2^31
+ * 16-byte pieces (32 GiB per tensor), else PA_ERR_INVALID_ARG.
  */
 int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
                      const void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
@@ -329,7 +331,8 @@ int gather_cached_kv(void* key_out, void* value_out, const void* key_cache,
  * share a slot (otherwise which row lands there is unspecified).
  * dtype: PA_F16, PA_BF16 or PA_FP8_E4M3 (bytes are moved, never converted).
  * A row (head_size elements) must be a multiple of 16 bytes; data pointers
- * 16-byte aligned.
+ * 16-byte aligned; fewer than 2^31 16-byte pieces of rows, as for
+ * gather_cached_kv.
  */
 int paged_kv_cache_write(void* key_cache, void* value_cache, const void* key, const void* value,
                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,

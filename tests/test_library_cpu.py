@@ -236,6 +236,13 @@ def test_gather_validation(L):
     assert g(FAKE + 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 0, 0, None) == ALIGN
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 4, 8, 128, 16, 10, 0, 0, None) == ALIGN
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 64, 128, 16, 10, 0, 0, None) == INVALID
+    # 2^31 16-byte pieces (2^24 tokens x 8 heads x 16 pieces), and just below 2^32: the
+    # kernels' 32-bit grid-stride counters could wrap around, so both are refused
+    for n in (1 << 24, (1 << 25) - 1):
+        assert g(FAKE, FAKE, FAKE, FAKE, FAKE, n, 8, 128, 16, 10, 0, 0, None) == INVALID
+        assert "too large" in L.pa_last_error().decode()
+        assert L.paged_kv_cache_write(FAKE, FAKE, FAKE, FAKE, FAKE, n, 8, 128, 16, 10, 0, 0,
+                                      None) == INVALID
     assert g(None, None, None, None, None, 0, 8, 128, 16, 10, 0, 0, None) == OK
 
 
