@@ -166,6 +166,7 @@ def _decode_structs(out, query, key_cache, value_cache, block_tables, context_le
         _require(alibi_slopes, "alibi_slopes", torch.float32)
     if qdt not in _DTYPE:
         raise ValueError(f"unsupported dtype {qdt}")
+    k_scale, v_scale, partition_size = float(k_scale), float(v_scale), int(partition_size)
     key = (query.shape, key_cache.shape, block_tables.shape[1], qdt, kdt, k_scale, v_scale, layout,
            partition_size, engine, schedule)
     structs = _decode_struct_cache.get(key)
