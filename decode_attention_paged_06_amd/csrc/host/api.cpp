@@ -150,7 +150,8 @@ CallShape decode_shape(const pa_dims* d) {
 }
 
 // Workspace of a split plan: fp32 partial outputs, then (m, l) pairs, then
-// (longest-first schedule only) the order of the num_seqs * P work units.
+// (longest-first schedule only) the order of the num_seqs * P work units and
+// one int32 counter.
 struct SplitLayout {
   size_t ml_offset = 0, order_offset = 0, bytes = 0;
 };
@@ -160,7 +161,8 @@ SplitLayout split_layout(const pa_dims* d, const CallShape& c, int P, bool longe
   const size_t rows = (size_t)c.rows * d->num_heads * P;
   w.ml_offset = align_up(rows * d->head_size * sizeof(float), kWsAlign);
   w.order_offset = align_up(w.ml_offset + rows * 2 * sizeof(float), kWsAlign);
-  w.bytes = longest_first ? w.order_offset + (size_t)d->num_seqs * P * sizeof(int32_t)
+  // (longest first) the order, then the start counter of the later workgroups
+  w.bytes = longest_first ? w.order_offset + ((size_t)d->num_seqs * P + 1) * sizeof(int32_t)
                           : w.ml_offset + rows * 2 * sizeof(float);
   return w;
 }
@@ -454,6 +456,19 @@ int run_attention(void* out, const void* query, const void* key_cache, const voi
   if (order != nullptr) {
     if ((long long)dims->num_kv_heads * a.row_chunks * dims->num_seqs * plan.num_partitions > 0x7fffffffLL)
       return fail(PA_ERR_INVALID_ARG, "too many work units for a longest-first schedule");
+    // staged decode with one workgroup per CU: the workgroups after the first
+    // round take their places in the order by start (a counter after the
+    // order); with several per CU it measured no faster (32-head groups) or
+    // 1% slower (64-head groups)
+    const int group = dims->num_heads / dims->num_kv_heads;
+    if (plan.engine == PA_ENGINE_MFMA && !c.multi && pa::mfma_head_tiles(group) > 1) {
+      int occ = 0, cus = 0;
+      if ((st = share_occupancy(dims, &occ)) || (st = current_num_cus(&cus))) return st;
+      if (occ == 1) {
+        a.ticket = order + (size_t)dims->num_seqs * plan.num_partitions;
+        a.static_wgs = cus;
+      }
+    }
     hipError_t e = pa::launch_unit_order(a, order, s);
     if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "schedule launch: %s", hipGetErrorString(e));
     a.unit_order = order;

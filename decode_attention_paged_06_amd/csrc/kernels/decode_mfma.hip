@@ -866,9 +866,26 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
       part = blockIdx.z;
       if (a.unit_order != nullptr) {  // longest-first schedule over a 1-D grid
         const int X = a.num_kv_heads * a.row_chunks;
-        const int n = blockIdx.x / X;
+        int b = blockIdx.x;
+        if constexpr (STAGE) {
+          // Workgroups of the first round (one per CU) keep their place; each
+          // later one takes the next place in the order of its start.  The
+          // hardware deals workgroups to the XCDs in turn, so by block index
+          // a slower XCD would get as many long units as a faster one; by
+          // start order, the CUs that free first take the longer remaining
+          // units whatever XCD they sit on (MQA 48/1 ragged batch 256: 103.8
+          // -> 98.6 us).  Places are unique and cover the rest of the order,
+          // so every unit is still walked exactly once.
+          if (a.ticket != nullptr && b >= a.static_wgs) {
+            int* tk = reinterpret_cast<int*>(toff_lds);  // (the table window is filled later)
+            if (threadIdx.x == 0) *tk = atomicAdd(a.ticket, 1);
+            __syncthreads();
+            b = a.static_wgs + __builtin_amdgcn_readfirstlane(*tk);
+          }
+        }
+        const int n = b / X;
         const int u = a.unit_order[n];
-        xi = blockIdx.x - n * X;
+        xi = b - n * X;
         seq = u % S;
         part = u / S;
       }

@@ -6,7 +6,8 @@
 // order as earlier ones retire, so starting the longest units first keeps the
 // tail of the launch short: the classic longest-processing-time-first list
 // schedule.  One workgroup buckets the units by token count (a counting sort
-// in LDS) and writes the order the decode kernel then follows.
+// in LDS) and writes the order the decode kernel then follows, and zeroes the
+// counter from which the decode's later workgroups take their places.
 #include "../launch.h"
 #include "device_common.h"
 
@@ -32,6 +33,7 @@ __global__ __launch_bounds__(kOrderThreads) void unit_order_kernel(const DecodeA
     return w == 0 ? kBuckets - 1 : (int)((long long)(ptok - w) * (kBuckets - 2) / ptok);
   };
   for (int b = threadIdx.x; b < kBuckets; b += kOrderThreads) count[b] = 0;
+  if (threadIdx.x == 0 && a.ticket != nullptr) *a.ticket = 0;
   __syncthreads();
   for (int u = threadIdx.x; u < n_units; u += kOrderThreads) atomicAdd(&count[bucket_of(u)], 1);
   __syncthreads();

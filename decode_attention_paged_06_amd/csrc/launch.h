@@ -48,6 +48,12 @@ struct DecodeArgs {
   // (sequence, partition) unit_order[b / (num_kv_heads * row_chunks)], encoded
   // partition * num_seqs + sequence.  nullptr = the grid's own order.
   const int32_t* unit_order = nullptr;
+  // (longest first, staged kernel) workgroups b >= static_wgs -- those that
+  // start as earlier ones retire -- take their place in that order from the
+  // counter at *ticket (zeroed by the order kernel) in the order they start,
+  // whatever XCD they run on
+  int32_t* ticket = nullptr;
+  int32_t static_wgs = 0;
   // Equal-share schedule (decode on the LDS-staged kernel): stream_wgs > 0
   // workgroups split the batch's tiles, walked item by item (item = kv head *
   // num_seqs + sequence, a sequence's tiles of min(16, block_size) tokens in

@@ -130,7 +130,10 @@ typedef enum {
  * its work out over workgroups.  GRID and LONGEST_FIRST cut each sequence into
  * fixed partitions, one workgroup each; with ragged context lengths these
  * units differ in size, and starting the longest first (a small ordering
- * kernel runs before the decode kernel) shortens the tail of the launch.
+ * kernel runs before the decode kernel) shortens the tail of the launch; on
+ * the LDS-staged kernel at one workgroup per CU, the workgroups after the
+ * first round take the remaining units in the order they start (a counter in
+ * the workspace), so CUs that free first take the longer ones.
  * GRID and LONGEST_FIRST give identical results.  EQUAL_SHARES (groups of
  * more than 16 heads, at most 2048 sequences): as many workgroups as the
  * device holds at once each walk an equal share of the batch's cache tiles,

@@ -363,8 +363,10 @@ def test_plan_schedule(L):
     assert st == OK and p.num_partitions > 1 and p.schedule == LONGEST
     st, g = plan(L, mqa, schedule=GRID)
     assert st == OK and g.schedule == GRID and g.num_partitions == p.num_partitions
-    # the unit order (one int32 per (sequence, partition)) sits after the partials
-    assert p.workspace_bytes >= g.workspace_bytes + 256 * p.num_partitions * 4
+    # the unit order (one int32 per (sequence, partition)) and the start counter of
+    # the later workgroups sit after the partials (256-byte aligned)
+    order_at = (g.workspace_bytes + 255) // 256 * 256
+    assert p.workspace_bytes == order_at + (256 * p.num_partitions + 1) * 4
     st, p = plan(L, dims(S=4))                             # split GQA: grid order unless asked
     assert st == OK and p.num_partitions > 1 and p.schedule == GRID
     st, p = plan(L, dims(S=4), schedule=LONGEST)
