@@ -17,6 +17,7 @@ namespace {
 
 constexpr int kOrderThreads = 1024;
 constexpr int kBuckets = 64;  // bucket 0: full partitions ... 62: shortest, 63: empty
+constexpr int kKeep = 4;      // units per thread whose bucket the second pass reuses
 
 __global__ __launch_bounds__(kOrderThreads) void unit_order_kernel(const DecodeArgs a, int32_t* order) {
   __shared__ int count[kBuckets];
@@ -35,7 +36,19 @@ __global__ __launch_bounds__(kOrderThreads) void unit_order_kernel(const DecodeA
   for (int b = threadIdx.x; b < kBuckets; b += kOrderThreads) count[b] = 0;
   if (threadIdx.x == 0 && a.ticket != nullptr) *a.ticket = 0;
   __syncthreads();
-  for (int u = threadIdx.x; u < n_units; u += kOrderThreads) atomicAdd(&count[bucket_of(u)], 1);
+  // the buckets of this thread's first kKeep units stay in registers for the
+  // second pass (one round trip to the lengths fewer)
+  int kept[kKeep];
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) {
+    const int u = threadIdx.x + k * kOrderThreads;
+    kept[k] = u < n_units ? bucket_of(u) : -1;
+  }
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k)
+    if (kept[k] >= 0) atomicAdd(&count[kept[k]], 1);
+  for (int u = threadIdx.x + kKeep * kOrderThreads; u < n_units; u += kOrderThreads)
+    atomicAdd(&count[bucket_of(u)], 1);
   __syncthreads();
   if (threadIdx.x == 0) {
     int sum = 0;
@@ -45,7 +58,11 @@ __global__ __launch_bounds__(kOrderThreads) void unit_order_kernel(const DecodeA
     }
   }
   __syncthreads();
-  for (int u = threadIdx.x; u < n_units; u += kOrderThreads) order[atomicAdd(&cursor[bucket_of(u)], 1)] = u;
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k)
+    if (kept[k] >= 0) order[atomicAdd(&cursor[kept[k]], 1)] = threadIdx.x + k * kOrderThreads;
+  for (int u = threadIdx.x + kKeep * kOrderThreads; u < n_units; u += kOrderThreads)
+    order[atomicAdd(&cursor[bucket_of(u)], 1)] = u;
 }
 
 }  // namespace
