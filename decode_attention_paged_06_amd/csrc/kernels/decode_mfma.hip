@@ -880,7 +880,10 @@ __global__ __launch_bounds__(NT * TG * 64) void decode_mfma_kernel(const DecodeA
             int* tk = reinterpret_cast<int*>(toff_lds);  // (the table window is filled later)
             if (threadIdx.x == 0) *tk = atomicAdd(a.ticket, 1);
             __syncthreads();
-            b = a.static_wgs + __builtin_amdgcn_readfirstlane(*tk);
+            // (a counter the ordering kernel did not clear could only give a
+            // wrong place, never one outside the grid)
+            const int t = __builtin_amdgcn_readfirstlane(*tk);
+            b = a.static_wgs + min(max(t, 0), (int)gridDim.x - 1 - a.static_wgs);
           }
         }
         const int n = b / X;
