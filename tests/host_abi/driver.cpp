@@ -121,6 +121,10 @@ static void mqa_longest_first() {
   CHECK(a.unit_order == g_launches[0].ptr);
   const char* order = reinterpret_cast<const char*>(a.unit_order);
   CHECK(order >= w && order + 256 * 2 * 4 <= w + ws);
+  // one 12-wave workgroup per CU: the workgroups after the first round take
+  // their places from the counter right after the order, in the workspace
+  CHECK(a.ticket == a.unit_order + 256 * 2 && reinterpret_cast<const char*>(a.ticket + 1) <= w + ws);
+  CHECK(a.static_wgs == kStubCus);
   CHECK(a.alibi == reinterpret_cast<const float*>(FAKE + 64));
 }
 
